@@ -1,0 +1,171 @@
+/*
+ * diffkv_attn.h - paged attention for models whose key and value head dims
+ * differ (QK 192, V 128), with grouped-query heads, on MI355X (gfx950).
+ *
+ * What the calls compute (the pages this library is built from):
+ *   - "sglang PR 41886, Default MiMo attention to FA4 on SM100", Accuracy
+ *     Tests: QK=192/V=128 attention, full and sliding-window layers with
+ *     sinks, single-token decode, 8-token verify, ragged page boundaries,
+ *     graph replay.
+ *   - "diffbot/MiMo-V2.6-Flash-RL-FP8KV-W4A8-2x-RTX-PRO-6000", What the
+ *     kernels do: split-KV for the multi-token verify step, 4096-token
+ *     prefill chunks at 26K context with 16 query heads per KV head, FP8
+ *     E4M3 K/V converted as it is loaded.
+ *   - "sglang PR 32818, Route asymmetric-KV models to fa4 on SM100": K and V
+ *     rows have different widths, so they live in two separate caches.
+ *
+ * For sequence b with L = seq_lens[b] and n = q_lens[b], new token i (packed
+ * row r0 + i, r0 = q_lens[0] + ... + q_lens[b-1]) sits at position
+ * p = L - n + i and, for query head h, attends over KV head g = h / G
+ * (G = num_q_heads / num_kv_heads) to the keys j with lo <= j <= p, where
+ * lo = 0 when window <= 0 and lo = max(0, p - window + 1) otherwise:
+ *     x_j  = softmax_scale * dot(q[r0+i, h, :], K_j)
+ *     out  = sum_j e^(x_j - m) V_j / (sum_j e^(x_j - m) + e^(s_h - m))
+ * with K_j = k_cache[block_table[b][j / P], j % P, g, :] * k_scale,
+ * V_j likewise with v_scale (scales apply to FP8 caches only; bf16 caches are
+ * used as stored), m the running maximum, and the sink term present only
+ * when sinks != NULL.  s_h is a logit in the already-scaled domain.
+ *
+ * All three entry points compute this same function; they differ only in
+ * how the work is cut up and in the q_len they accept.
+ */
+#ifndef DIFFKV_ATTN_H
+#define DIFFKV_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  No exception ever crosses this interface. */
+enum {
+  DIFFKV_OK = 0,
+  DIFFKV_INVALID_ARGUMENT = 1,   /* null required pointer, bad size or bound   */
+  DIFFKV_UNSUPPORTED = 2,        /* head dims, page size or dtype not built     */
+  DIFFKV_WORKSPACE_TOO_SMALL = 3,/* workspace_bytes below diffkv_attn_workspace_bytes */
+  DIFFKV_HIP_ERROR = 4           /* a launch failed (hipGetLastError)           */
+};
+
+/* Entry selectors for diffkv_attn_workspace_bytes / diffkv_attn_validate. */
+enum { DIFFKV_ENTRY_DECODE = 0, DIFFKV_ENTRY_VERIFY = 1, DIFFKV_ENTRY_PREFILL = 2 };
+
+/* K/V storage formats. */
+enum {
+  DIFFKV_KV_BF16 = 0,            /* bfloat16                                    */
+  DIFFKV_KV_FP8_E4M3 = 1         /* OCP FP8 E4M3FN (bias 7, max 448, NaN 0x7F/0xFF) */
+};
+
+/*
+ * Shape descriptor.  Every field is a host-side value; the launch grid is
+ * derived from these bounds only, never from device data, so a call can be
+ * captured in a HIP graph and replayed with new device contents of seq_lens,
+ * q_lens and block_table as long as they stay within these bounds.
+ */
+typedef struct diffkv_attn_desc {
+  int32_t batch;               /* number of sequences B >= 1                        */
+  int32_t num_q_heads;         /* Hq >= 1                                           */
+  int32_t num_kv_heads;        /* Hkv >= 1, Hq % Hkv == 0, G = Hq / Hkv <= 16        */
+  int32_t head_dim_qk;         /* must be 192                                       */
+  int32_t head_dim_v;          /* must be 128                                       */
+  int32_t page_size;           /* P: a power of two in [1, 256]                     */
+  int32_t num_pages;           /* pages in each cache                               */
+  int32_t block_table_stride;  /* int32 entries per block-table row                 */
+  int32_t max_seq_len;         /* >= every seq_lens[b]                              */
+  int32_t max_q_len;           /* >= every q_lens[b]; 1 for decode, <= 16 for verify */
+  int32_t total_q;             /* == sum of q_lens: rows of q and out               */
+  int32_t kv_dtype;            /* DIFFKV_KV_BF16 or DIFFKV_KV_FP8_E4M3              */
+  int32_t force_num_splits;    /* 0 = automatic; > 0 forces the key-axis split count
+                                  (decode/verify only; a test hook)                 */
+} diffkv_attn_desc;
+
+/*
+ * Attention over the paged cache.  Layouts (all row-major, contiguous):
+ *   q            bf16  [total_q, Hq, 192]; sequence b's rows start at r0
+ *   k_cache      bf16 or E4M3 [num_pages, P, Hkv, 192]
+ *   v_cache      bf16 or E4M3 [num_pages, P, Hkv, 128]
+ *   block_table  int32 [batch, block_table_stride]; entry t is the physical
+ *                page of the sequence's tokens [t*P, (t+1)*P).  Only entries
+ *                of pages holding a visible key are read; the others (pages
+ *                past the end, pages wholly before the window) may hold any
+ *                value, e.g. -1.
+ *   seq_lens     int32 [batch], tokens in the cache including the new ones
+ *   q_lens       int32 [batch], new tokens per sequence; NULL means all 1
+ *   window       keys visible to a token: the `window` newest up to and
+ *                including itself; <= 0 means full attention
+ *   sinks        fp32 [Hq] per-query-head sink logits, or NULL
+ *   k_scale, v_scale  per-tensor dequantisation scales (FP8 caches only)
+ *   softmax_scale     multiplies q.k before the softmax
+ *   out          bf16  [total_q, Hq, 128], written (round to nearest even)
+ *   lse_out      fp32  [total_q, Hq] natural-log log-sum-exp of the key
+ *                logits (sink excluded), or NULL
+ *   count_out    int32 [total_q, Hq]: number of keys each row combined, or
+ *                NULL (a check on which slots are read; costs time)
+ *   workspace    device scratch of at least diffkv_attn_workspace_bytes(desc,
+ *                entry) bytes, or NULL when that is 0; clobbered
+ *   stream       HIP stream every kernel is enqueued on, in order
+ *
+ * Ownership: every pointer is caller-owned device memory; the library keeps
+ * no reference after returning, never allocates, frees or synchronises, and
+ * never reads device data on the host.  out must not alias an input.
+ *
+ * Preconditions on device data (undefined behaviour if broken):
+ *   1 <= q_lens[b] <= seq_lens[b] <= max_seq_len, q_lens[b] <= max_q_len,
+ *   sum(q_lens) == total_q, and every block-table entry that is read lies in
+ *   [0, num_pages).  Slots the rows cannot see may hold anything, NaN
+ *   included; it never reaches the output.
+ *
+ * Returns DIFFKV_OK, or a status from the enum above (synchronous checks of
+ * the descriptor and pointers, or a launch failure).  Faults in device code
+ * surface as HIP errors at the caller's next synchronisation.
+ *
+ * diffkv_attn_decode:  max_q_len must be 1 (single-token decode, split-KV).
+ * diffkv_attn_verify:  max_q_len <= 16 (speculative verify block, causal
+ *                      within the block, split-KV so long contexts fill the
+ *                      GPU, as the split-KV fix for the verify step does).
+ * diffkv_attn_prefill: any q_len (chunked causal prefill over a paged prefix,
+ *                      large query tiles on the matrix cores).
+ */
+int diffkv_attn_decode(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* q_lens, int32_t window, const float* sinks, float k_scale,
+                       float v_scale, float softmax_scale, void* out, float* lse_out,
+                       int32_t* count_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+int diffkv_attn_verify(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* q_lens, int32_t window, const float* sinks, float k_scale,
+                       float v_scale, float softmax_scale, void* out, float* lse_out,
+                       int32_t* count_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+int diffkv_attn_prefill(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                        const int32_t* q_lens, int32_t window, const float* sinks, float k_scale,
+                        float v_scale, float softmax_scale, void* out, float* lse_out,
+                        int32_t* count_out, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* Bytes of workspace the entry needs for this descriptor (0 when none).
+ * Host only; depends on the descriptor alone.  Returns 0 for an invalid
+ * descriptor (check diffkv_attn_validate). */
+size_t diffkv_attn_workspace_bytes(const diffkv_attn_desc* desc, int entry);
+
+/* Synchronous check of a descriptor for an entry; host only, no HIP call. */
+int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry);
+
+/* Number of key-axis splits the entry would launch for this descriptor
+ * (1 for prefill).  Host only. */
+int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry);
+
+/* Static text for a status code. */
+const char* diffkv_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFKV_ATTN_H */

@@ -1,0 +1,227 @@
+"""Paged attention with asymmetric head dims, computed from its definition in float64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Definition (one query head h, one new query token; the readings of points the
+pages leave open are listed after it):
+
+  For sequence b with L = seq_lens[b] cached tokens (the new tokens included)
+  and n = q_lens[b] new tokens starting at packed row r0 = sum(q_lens[:b]),
+  new token i in [0, n) sits at position p = L - n + i.
+  Query head h reads KV head g = h // G with G = Hq / Hkv (contiguous GQA
+  groups; "diffbot/MiMo-V2.6-Flash-RL-FP8KV-W4A8-2x-RTX-PRO-6000", What the
+  kernels do, groups 16 query heads per KV head).
+  Visible keys: lo <= j <= p, with lo = 0 for full attention and
+  lo = max(0, p - W + 1) for a sliding window of W tokens (the token itself
+  included); causal within the verify block ("sglang PR 41886", Accuracy
+  Tests: full attention and SWA with sinks, decode, 8-token verify).
+  Key j lives in physical page block_table[b][j // P] at slot j % P; K and V
+  sit in two separate caches because their row widths differ (192 vs 128,
+  "sglang PR 32818", the trtllm_mha failure it fixes).
+      K_j = dec(k_cache[page, slot, g, :]) * k_scale     (192 values)
+      V_j = dec(v_cache[page, slot, g, :]) * v_scale     (128 values)
+  The scales multiply only FP8 caches (per-tensor dequantisation); bf16
+  caches are used as stored.
+      x_j = softmax_scale * sum_d q[r0 + i, h, d] * K_j[d]
+      m   = max(max_j x_j, s_h)         (s_h only when sinks are given)
+      den = sum_j exp(x_j - m) + exp(s_h - m)
+      out = sum_j exp(x_j - m) V_j / den
+      lse = m + ln sum_j exp(x_j - m)     (keys only; the sink is excluded)
+      count = number of visible keys
+
+Readings where the pages are silent (each the plainest one the text allows):
+  * seq_lens counts the new tokens, whose K/V are already in the cache.
+  * the verify mask is plain causal (linear draft chains, no trees).
+  * a window of W keeps the W newest keys including the token itself;
+    W <= 0 means full attention.
+  * a sink s_h is one fp32 logit per query head in the already-scaled logit
+    domain; it adds exp(s_h) to the denominator only and carries no value.
+  * lse uses the natural log and excludes the sink.
+Parity unpinned: the bf16 rounding pattern of a GPU output (compared within
+the tolerance only); the window and sink conventions above are readings, not
+statements of the pages.
+
+Split mode (`split=k` or `split="page"`) evaluates the same rows by cutting
+each (sequence, KV head) key range into pieces, computing (max, sum, output)
+per piece and merging by log-sum-exp, as split-KV does ("diffbot/...", What
+the kernels do: split-KV for the verify step).  It exists to pin the merge
+arithmetic; the result must equal the unsplit one to rounding.
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .codecs import decode_bf16, decode_e4m3fn
+
+
+@dataclass
+class OracleResult:
+    out: np.ndarray     # float64 [T, Hq, Dv]
+    lse: np.ndarray     # float64 [T, Hq]
+    count: np.ndarray   # int64   [T, Hq]
+    tokens: np.ndarray  # int64   [T], the packed query-token rows computed
+
+
+def _decode_cache(raw, kv_dtype, scale):
+    if kv_dtype == "bf16":
+        return decode_bf16(raw)
+    if kv_dtype == "fp8":
+        return decode_e4m3fn(raw) * float(scale)
+    raise ValueError(f"unknown kv dtype {kv_dtype!r}")
+
+
+def _piece_edges(j0, j1, split, page_size):
+    """Edges of the key pieces over the inclusive range [j0, j1]."""
+    if split is None:
+        return np.array([j0, j1 + 1], dtype=np.int64)
+    if split == "page":
+        inner = np.arange((j0 // page_size + 1) * page_size, j1 + 1, page_size, dtype=np.int64)
+        return np.concatenate([[j0], inner, [j1 + 1]]).astype(np.int64)
+    k = int(split)
+    if k < 1:
+        raise ValueError("split must be >= 1")
+    return np.round(np.linspace(j0, j1 + 1, k + 1)).astype(np.int64)
+
+
+def _direct(x, V, s_h):
+    """The definition itself: one max, one denominator, one weighted sum.
+
+    x [ni, G, nj] scaled scores with invisible keys at -inf; V [nj, Dv];
+    s_h [G] sink logits or None.
+    """
+    m = x.max(axis=2)                                                # [ni, G]
+    if s_h is not None:
+        m = np.maximum(m, s_h[None, :])
+    e = np.where(np.isfinite(x), np.exp(x - m[:, :, None]), 0.0)    # exp(-inf) -> 0
+    key_sum = e.sum(axis=2)
+    den = key_sum + (0.0 if s_h is None else np.exp(s_h[None, :] - m))
+    o = np.matmul(e, V) / den[:, :, None]
+    with np.errstate(divide="ignore"):
+        return o, m + np.log(key_sum)
+
+
+def _pieces_merged(x, V, s_h, edges):
+    """Split-KV evaluation: per piece (max, sum, normalised output), merged by
+    log-sum-exp with the sink joining the merged denominator."""
+    piece_lse, piece_out = [], []
+    for e0, e1 in zip(edges[:-1], edges[1:]):
+        if e1 <= e0:
+            continue
+        xs = x[:, :, e0:e1]
+        m = xs.max(axis=2)                                            # -inf if none visible
+        m_safe = np.where(np.isfinite(m), m, 0.0)
+        w = np.where(np.isfinite(xs), np.exp(xs - m_safe[:, :, None]), 0.0)
+        l = w.sum(axis=2)
+        o = np.matmul(w, V[e0:e1])
+        with np.errstate(invalid="ignore", divide="ignore"):
+            piece_out.append(np.where(l[:, :, None] > 0, o / l[:, :, None], 0.0))
+            piece_lse.append(np.where(l > 0, m_safe + np.log(l), -np.inf))
+    pl = np.stack(piece_lse)                                          # [S, ni, G]
+    po = np.stack(piece_out)                                          # [S, ni, G, Dv]
+    M = pl.max(axis=0)
+    if s_h is not None:
+        M = np.maximum(M, s_h[None, :])
+    wts = np.where(np.isfinite(pl), np.exp(pl - M[None]), 0.0)
+    key_sum = wts.sum(axis=0)
+    den = key_sum + (0.0 if s_h is None else np.exp(s_h[None, :] - M))
+    o = (wts[..., None] * po).sum(axis=0) / den[..., None]
+    with np.errstate(divide="ignore"):
+        return o, M + np.log(key_sum)
+
+
+def paged_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens=None, *,
+                    num_q_heads, num_kv_heads, kv_dtype, softmax_scale,
+                    window=0, sinks=None, k_scale=1.0, v_scale=1.0,
+                    tokens=None, split=None, max_chunk_elems=1 << 22):
+    """Evaluate the definition above.
+
+    q            uint16 [total_q, Hq, Dqk]         bf16 codes
+    k_cache      uint16|uint8 [pages, P, Hkv, Dqk] bf16 codes or E4M3FN codes
+    v_cache      uint16|uint8 [pages, P, Hkv, Dv]
+    block_table  int   [B, stride]
+    seq_lens     int   [B]
+    q_lens       int   [B] or None (all 1)
+    sinks        float [Hq] or None
+    tokens       optional iterable of packed query rows to compute (default all)
+    """
+    q = np.asarray(q)
+    k_cache = np.asarray(k_cache)
+    v_cache = np.asarray(v_cache)
+    block_table = np.asarray(block_table)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    B = seq_lens.shape[0]
+    q_lens = np.ones(B, dtype=np.int64) if q_lens is None else np.asarray(q_lens, dtype=np.int64)
+    Hq, Hkv = int(num_q_heads), int(num_kv_heads)
+    if Hq % Hkv != 0:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    G = Hq // Hkv
+    num_pages, P = k_cache.shape[0], k_cache.shape[1]
+    Dqk, Dv = k_cache.shape[3], v_cache.shape[3]
+    total_q = int(q_lens.sum())
+    if q.shape != (total_q, Hq, Dqk):
+        raise ValueError(f"q shape {q.shape} != {(total_q, Hq, Dqk)}")
+    W = int(window)
+    sink = None if sinks is None else np.asarray(sinks, dtype=np.float64)
+
+    starts = np.concatenate([[0], np.cumsum(q_lens)[:-1]]).astype(np.int64)
+    if tokens is None:
+        want = np.arange(total_q, dtype=np.int64)
+    else:
+        want = np.unique(np.asarray(tokens, dtype=np.int64))
+    T = want.shape[0]
+    out = np.full((T, Hq, Dv), np.nan)
+    lse = np.full((T, Hq), np.nan)
+    count = np.zeros((T, Hq), dtype=np.int64)
+    row_of = {int(t): r for r, t in enumerate(want)}
+
+    for b in range(B):
+        L, n, r0 = int(seq_lens[b]), int(q_lens[b]), int(starts[b])
+        if not (1 <= n <= L):
+            raise ValueError(f"sequence {b}: need 1 <= q_len ({n}) <= seq_len ({L})")
+        local = np.array([t - r0 for t in want if r0 <= t < r0 + n], dtype=np.int64)
+        if local.size == 0:
+            continue
+        p_all = L - n + local
+        lo_all = np.maximum(0, p_all - W + 1) if W > 0 else np.zeros_like(p_all)
+
+        # Union key range of the requested tokens; only its pages are read.
+        j0, j1 = int(lo_all.min()), int(p_all.max())
+        j = np.arange(j0, j1 + 1, dtype=np.int64)
+        page_index = j // P
+        phys = block_table[b, page_index].astype(np.int64)
+        if phys.min() < 0 or phys.max() >= num_pages:
+            raise ValueError(f"sequence {b}: block-table entry out of range for a visible page")
+        slot = j % P
+
+        # Rows per chunk so one score block stays near max_chunk_elems values.
+        per_tok = max(1, G * j.size)
+        step = max(1, max_chunk_elems // per_tok)
+        edges = _piece_edges(j0, j1, split, P) - j0
+
+        for g in range(Hkv):
+            K = _decode_cache(k_cache[phys, slot, g, :], kv_dtype, k_scale)   # [nj, Dqk]
+            V = _decode_cache(v_cache[phys, slot, g, :], kv_dtype, v_scale)   # [nj, Dv]
+            heads = np.arange(g * G, (g + 1) * G)
+            s_h = None if sink is None else sink[heads]                     # [G]
+            for c0 in range(0, local.size, step):
+                li = local[c0:c0 + step]
+                p = p_all[c0:c0 + step]
+                lo = lo_all[c0:c0 + step]
+                Q = decode_bf16(q[r0 + li][:, heads, :])                      # [ni, G, Dqk]
+                vis = (j[None, :] >= lo[:, None]) & (j[None, :] <= p[:, None])  # [ni, nj]
+                x = softmax_scale * np.matmul(Q, K.T)                        # [ni, G, nj]
+                x = np.where(vis[:, None, :], x, -np.inf)
+
+                if split is None:
+                    o, row_lse = _direct(x, V, s_h)
+                else:
+                    o, row_lse = _pieces_merged(x, V, s_h, edges)
+
+                cnt = vis.sum(axis=1)
+                for a, t in enumerate(li):
+                    r = row_of[int(r0 + t)]
+                    out[r, heads, :] = o[a]
+                    lse[r, heads] = row_lse[a]
+                    count[r, heads] = cnt[a]
+    return OracleResult(out=out, lse=lse, count=count, tokens=want)

@@ -1,0 +1,122 @@
+"""ctypes binding of libdiffkv_attn.so: the C-ABI entry points under the same names.
+
+Argument marshalling only.  Tensors are passed as raw device pointers and the
+stream as torch's current HIP stream; every step of the computation runs in
+the library's kernels.  There is no fallback: if the library is missing,
+every call raises.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = range(5)
+ENTRY_DECODE, ENTRY_VERIFY, ENTRY_PREFILL = 0, 1, 2
+KV_BF16, KV_FP8_E4M3 = 0, 1
+ENTRIES = {"decode": ENTRY_DECODE, "verify": ENTRY_VERIFY, "prefill": ENTRY_PREFILL}
+
+
+class DiffKVError(RuntimeError):
+    pass
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "batch", "num_q_heads", "num_kv_heads", "head_dim_qk", "head_dim_v", "page_size",
+        "num_pages", "block_table_stride", "max_seq_len", "max_q_len", "total_q", "kv_dtype",
+        "force_num_splits")]
+
+
+def library_path():
+    return os.path.join(_HERE, "libdiffkv_attn.so")
+
+
+_ENTRY_ARGS = [ctypes.POINTER(AttnDesc)] + [ctypes.c_void_p] * 6 + [
+    ctypes.c_int32, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+    ctypes.c_void_p]
+
+
+def load_library():
+    """Open the HIP library once; raise if it is not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise DiffKVError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    for name in ("diffkv_attn_decode", "diffkv_attn_verify", "diffkv_attn_prefill"):
+        fn = getattr(lib, name)
+        fn.argtypes = _ENTRY_ARGS
+        fn.restype = ctypes.c_int
+    lib.diffkv_attn_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int]
+    lib.diffkv_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.diffkv_attn_validate.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int]
+    lib.diffkv_attn_validate.restype = ctypes.c_int
+    lib.diffkv_attn_num_splits.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int]
+    lib.diffkv_attn_num_splits.restype = ctypes.c_int
+    lib.diffkv_attn_strerror.argtypes = [ctypes.c_int]
+    lib.diffkv_attn_strerror.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _ptr(x):
+    """Device address of a tensor (or an int address, or None -> NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def diffkv_attn_strerror(status):
+    return load_library().diffkv_attn_strerror(int(status)).decode()
+
+
+def diffkv_attn_validate(desc, entry):
+    return int(load_library().diffkv_attn_validate(ctypes.byref(desc), int(entry)))
+
+
+def diffkv_attn_workspace_bytes(desc, entry):
+    return int(load_library().diffkv_attn_workspace_bytes(ctypes.byref(desc), int(entry)))
+
+
+def diffkv_attn_num_splits(desc, entry):
+    return int(load_library().diffkv_attn_num_splits(ctypes.byref(desc), int(entry)))
+
+
+def _call(name, desc, q, k_cache, v_cache, block_table, seq_lens, q_lens, window, sinks,
+          k_scale, v_scale, softmax_scale, out, lse_out=None, count_out=None, workspace=None,
+          workspace_bytes=0, stream=None):
+    fn = getattr(load_library(), name)
+    status = fn(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                _ptr(seq_lens), _ptr(q_lens), int(window), _ptr(sinks), float(k_scale),
+                float(v_scale), float(softmax_scale), _ptr(out), _ptr(lse_out), _ptr(count_out),
+                _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if status != OK:
+        raise DiffKVError(f"{name}: {diffkv_attn_strerror(status)} (status {status})")
+
+
+def diffkv_attn_decode(*args, **kwargs):
+    _call("diffkv_attn_decode", *args, **kwargs)
+
+
+def diffkv_attn_verify(*args, **kwargs):
+    _call("diffkv_attn_verify", *args, **kwargs)
+
+
+def diffkv_attn_prefill(*args, **kwargs):
+    _call("diffkv_attn_prefill", *args, **kwargs)
