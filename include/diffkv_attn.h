@@ -67,7 +67,7 @@ enum {
 typedef struct diffkv_attn_desc {
   int32_t batch;               /* number of sequences B >= 1                        */
   int32_t num_q_heads;         /* Hq >= 1                                           */
-  int32_t num_kv_heads;        /* Hkv >= 1, Hq % Hkv == 0, G = Hq / Hkv <= 16        */
+  int32_t num_kv_heads;        /* Hkv >= 1, Hq % Hkv == 0, G = Hq / Hkv             */
   int32_t head_dim_qk;         /* must be 192                                       */
   int32_t head_dim_v;          /* must be 128                                       */
   int32_t page_size;           /* P: a power of two in [1, 256]                     */
@@ -157,9 +157,9 @@ size_t diffkv_attn_workspace_bytes(const diffkv_attn_desc* desc, int entry);
 /* Synchronous check of a descriptor for an entry; host only, no HIP call. */
 int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry);
 
-/* Number of key-axis splits the entry would launch for this descriptor
- * (1 for prefill).  Host only. */
-int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry);
+/* Number of key-axis splits the entry launches for this descriptor and
+ * window (1 for prefill; 0 for an invalid descriptor).  Host only. */
+int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window);
 
 /* Static text for a status code. */
 const char* diffkv_attn_strerror(int status);

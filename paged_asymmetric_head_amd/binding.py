@@ -56,7 +56,7 @@ def load_library():
     lib.diffkv_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.diffkv_attn_validate.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int]
     lib.diffkv_attn_validate.restype = ctypes.c_int
-    lib.diffkv_attn_num_splits.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int]
+    lib.diffkv_attn_num_splits.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int, ctypes.c_int32]
     lib.diffkv_attn_num_splits.restype = ctypes.c_int
     lib.diffkv_attn_strerror.argtypes = [ctypes.c_int]
     lib.diffkv_attn_strerror.restype = ctypes.c_char_p
@@ -94,8 +94,8 @@ def diffkv_attn_workspace_bytes(desc, entry):
     return int(load_library().diffkv_attn_workspace_bytes(ctypes.byref(desc), int(entry)))
 
 
-def diffkv_attn_num_splits(desc, entry):
-    return int(load_library().diffkv_attn_num_splits(ctypes.byref(desc), int(entry)))
+def diffkv_attn_num_splits(desc, entry, window=0):
+    return int(load_library().diffkv_attn_num_splits(ctypes.byref(desc), int(entry), int(window)))
 
 
 def _call(name, desc, q, k_cache, v_cache, block_table, seq_lens, q_lens, window, sinks,

@@ -1,0 +1,50 @@
+"""Builds libdiffkv_attn.so in-tree with hipcc for gfx950.
+
+    python -m paged_asymmetric_head_amd.build
+
+Every run recompiles (no staleness check).  Packed-FP32 VALU forms are
+switched off for the device pass.
+"""
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OUTPUT = os.path.join(HERE, "libdiffkv_attn.so")
+SOURCES = [os.path.join(CSRC, "diffkv_attn.hip")]
+ARCH = "gfx950"
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    return "hipcc"
+
+
+def command(output=OUTPUT, extra=()):
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}",
+            *extra, "-o", output, *SOURCES]
+
+
+def build(verbose=False):
+    tmp = OUTPUT + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+    os.replace(tmp, OUTPUT)
+    return OUTPUT
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,76 @@
+// Device helpers shared by the gfx950 attention kernels: vector types, MFMA
+// wrappers, storage-format conversion and wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace diffkv {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// S/O tiles: D(16x16, fp32) += A(16 x K) * B(K x 16) on the matrix cores.
+// Operand layout shared by both shapes: lane l supplies row (l % 16) of A and
+// column (l % 16) of B, its lane group (l / 16) a slice of the contraction;
+// D comes back as rows 4*(l/16)+i, column l%16 for i = 0..3.
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> bf16, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = static_cast<__bf16>(lo);
+  __bf16 b = static_cast<__bf16>(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Four OCP E4M3FN codes (one 32-bit word, byte 0 first) -> four bf16 codes in
+// two words.  The hardware converter yields the exact fp32 value (NaN codes
+// give NaN); every finite E4M3 value has at most 4 significant bits and an
+// exponent in [-9, 8], so dropping the low 16 bits of the fp32 is exact.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  u32x2 r;
+  r.x = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u);
+  r.y = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u);
+  return r;
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Packed query row where sequence b starts: sum of q_lens[0..b).  One wave
+// computes it cooperatively (a strided sum and a wave reduction).
+__device__ __forceinline__ int seq_row_start(const int32_t* q_lens, int b) {
+  if (q_lens == nullptr) return b;
+  int s = 0;
+  for (int k = lane_id(); k < b; k += 64) s += q_lens[k];
+  return wave_sum_int(s);
+}
+
+}  // namespace diffkv

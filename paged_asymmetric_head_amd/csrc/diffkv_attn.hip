@@ -1,0 +1,223 @@
+// C ABI of the paged asymmetric-head attention library: argument checks,
+// launch planning and kernel dispatch onto the caller's stream.
+//
+// The host side never allocates, frees, synchronises or reads device memory;
+// it derives every launch from the descriptor, so calls can be captured in a
+// HIP graph.  Errors are status codes; no exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "diffkv_attn.h"
+#include "plan.hpp"
+#include "split_attn.hpp"
+
+using namespace diffkv;
+
+namespace {
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+int validate_desc(const diffkv_attn_desc* d, int entry) {
+  if (d == nullptr) return DIFFKV_INVALID_ARGUMENT;
+  if (entry < DIFFKV_ENTRY_DECODE || entry > DIFFKV_ENTRY_PREFILL) return DIFFKV_INVALID_ARGUMENT;
+  if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1) return DIFFKV_INVALID_ARGUMENT;
+  if (d->num_q_heads % d->num_kv_heads != 0) return DIFFKV_INVALID_ARGUMENT;
+  if (d->head_dim_qk != kHeadDimQK || d->head_dim_v != kHeadDimV) return DIFFKV_UNSUPPORTED;
+  if (!is_pow2(d->page_size) || d->page_size > 256) return DIFFKV_UNSUPPORTED;
+  if (d->kv_dtype != DIFFKV_KV_BF16 && d->kv_dtype != DIFFKV_KV_FP8_E4M3) return DIFFKV_UNSUPPORTED;
+  if (d->num_pages < 1 || d->max_seq_len < 1 || d->max_q_len < 1 || d->total_q < 1)
+    return DIFFKV_INVALID_ARGUMENT;
+  if (d->max_q_len > d->max_seq_len) return DIFFKV_INVALID_ARGUMENT;
+  if ((long long)d->block_table_stride * d->page_size < d->max_seq_len) return DIFFKV_INVALID_ARGUMENT;
+  if (d->total_q < d->batch || (long long)d->total_q > (long long)d->batch * d->max_q_len)
+    return DIFFKV_INVALID_ARGUMENT;
+  if (d->force_num_splits < 0) return DIFFKV_INVALID_ARGUMENT;
+  if (entry == DIFFKV_ENTRY_DECODE && d->max_q_len != 1) return DIFFKV_INVALID_ARGUMENT;
+  if (entry == DIFFKV_ENTRY_VERIFY && d->max_q_len > 16) return DIFFKV_INVALID_ARGUMENT;
+  // Launch-shape limits.
+  if ((long long)d->batch * d->num_kv_heads > kMaxGridYZ) return DIFFKV_UNSUPPORTED;
+  {
+    const SplitPlan p = plan_split(*d, 0, entry != DIFFKV_ENTRY_PREFILL);
+    if (p.n_qtiles > kMaxGridYZ) return DIFFKV_UNSUPPORTED;
+  }
+  if ((long long)d->total_q * d->num_q_heads > (1LL << 31) / kHeadDimQK) return DIFFKV_UNSUPPORTED;
+  return DIFFKV_OK;
+}
+
+template <bool FP8, int RT, bool DIRECT, bool COUNT>
+hipError_t launch_split_kernel(const SplitArgs& a, dim3 grid, hipStream_t stream) {
+  void* args[] = {const_cast<SplitArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&split_attn_kernel<FP8, RT, DIRECT, COUNT>),
+                         grid, dim3(256), args, 0, stream);
+}
+
+template <bool FP8, int RT>
+hipError_t dispatch_split_rt(const SplitArgs& a, dim3 grid, bool direct, bool count, hipStream_t st) {
+  if (direct) return count ? launch_split_kernel<FP8, RT, true, true>(a, grid, st)
+                           : launch_split_kernel<FP8, RT, true, false>(a, grid, st);
+  return count ? launch_split_kernel<FP8, RT, false, true>(a, grid, st)
+               : launch_split_kernel<FP8, RT, false, false>(a, grid, st);
+}
+
+template <bool FP8>
+hipError_t dispatch_split(const SplitArgs& a, int rt, dim3 grid, bool direct, bool count,
+                          hipStream_t st) {
+  switch (rt) {
+    case 1: return dispatch_split_rt<FP8, 1>(a, grid, direct, count, st);
+    case 2: return dispatch_split_rt<FP8, 2>(a, grid, direct, count, st);
+    default: return dispatch_split_rt<FP8, 4>(a, grid, direct, count, st);
+  }
+}
+
+hipError_t launch_merge(const SplitArgs& a, int rows, dim3 grid, hipStream_t stream) {
+  void* args[] = {const_cast<SplitArgs*>(&a)};
+  const void* fn = rows == 16 ? reinterpret_cast<const void*>(&split_merge_kernel<16>)
+                 : rows == 32 ? reinterpret_cast<const void*>(&split_merge_kernel<32>)
+                              : reinterpret_cast<const void*>(&split_merge_kernel<64>);
+  return hipLaunchKernel(fn, grid, dim3(64), args, 0, stream);
+}
+
+hipError_t launch_fill(int32_t* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  int32_t zero = 0;
+  void* args[] = {&p, &n, &zero};
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fill_i32_kernel), dim3(blocks), dim3(256),
+                         args, 0, stream);
+}
+
+int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k_cache,
+              const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+              const int32_t* q_lens, int32_t window, const float* sinks, float k_scale,
+              float v_scale, float softmax_scale, void* out, float* lse_out, int32_t* count_out,
+              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = validate_desc(d, entry);
+  if (st != DIFFKV_OK) return st;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return DIFFKV_INVALID_ARGUMENT;
+  if (!q_lens && d->max_q_len != 1) return DIFFKV_INVALID_ARGUMENT;
+  if (!std::isfinite(softmax_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return DIFFKV_INVALID_ARGUMENT;
+
+  const bool fp8 = d->kv_dtype == DIFFKV_KV_FP8_E4M3;
+  const float ks = fp8 ? k_scale : 1.f;
+  const float vs = fp8 ? v_scale : 1.f;
+  const int G = d->num_q_heads / d->num_kv_heads;
+
+  if (count_out) {
+    const hipError_t e = launch_fill(count_out, (size_t)d->total_q * d->num_q_heads, stream);
+    if (e != hipSuccess) return DIFFKV_HIP_ERROR;
+  }
+
+  // Prefill runs one split per query tile (its many query rows fill the GPU).
+  const SplitPlan plan = plan_split(*d, window, entry != DIFFKV_ENTRY_PREFILL);
+  if (plan.num_splits > 1 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+    return DIFFKV_WORKSPACE_TOO_SMALL;
+
+  SplitArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.q_lens = q_lens;
+  a.sinks = sinks;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse_out = lse_out;
+  a.count_out = count_out;
+  if (plan.num_splits > 1) {
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          ((plan.part_o_bytes + 255) / 256) * 256);
+  }
+  a.hq = d->num_q_heads;
+  a.hkv = d->num_kv_heads;
+  a.group = G;
+  a.log2_page = ilog2(d->page_size);
+  a.bt_stride = d->block_table_stride;
+  a.window = window;
+  a.n_qtiles = plan.n_qtiles;
+  a.num_splits = plan.num_splits;
+  a.scale_log2 = softmax_scale * ks * kLog2e;
+  a.v_scale = vs;
+
+  const dim3 grid(plan.num_splits, plan.n_qtiles, d->batch * d->num_kv_heads);
+  const bool direct = plan.num_splits == 1;
+  hipError_t e = fp8 ? dispatch_split<true>(a, plan.row_tiles, grid, direct, count_out != nullptr, stream)
+                     : dispatch_split<false>(a, plan.row_tiles, grid, direct, count_out != nullptr, stream);
+  if (e == hipSuccess && !direct)
+    e = launch_merge(a, plan.rows, dim3(plan.n_qtiles * plan.rows, d->batch * d->num_kv_heads), stream);
+  return e == hipSuccess ? DIFFKV_OK : DIFFKV_HIP_ERROR;
+}
+
+}  // namespace
+
+extern "C" {
+
+int diffkv_attn_decode(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* q_lens, int32_t window, const float* sinks, float k_scale,
+                       float v_scale, float softmax_scale, void* out, float* lse_out,
+                       int32_t* count_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  return run_entry(DIFFKV_ENTRY_DECODE, desc, q, k_cache, v_cache, block_table, seq_lens, q_lens,
+                   window, sinks, k_scale, v_scale, softmax_scale, out, lse_out, count_out,
+                   workspace, workspace_bytes, stream);
+}
+
+int diffkv_attn_verify(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* q_lens, int32_t window, const float* sinks, float k_scale,
+                       float v_scale, float softmax_scale, void* out, float* lse_out,
+                       int32_t* count_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  return run_entry(DIFFKV_ENTRY_VERIFY, desc, q, k_cache, v_cache, block_table, seq_lens, q_lens,
+                   window, sinks, k_scale, v_scale, softmax_scale, out, lse_out, count_out,
+                   workspace, workspace_bytes, stream);
+}
+
+int diffkv_attn_prefill(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                        const int32_t* q_lens, int32_t window, const float* sinks, float k_scale,
+                        float v_scale, float softmax_scale, void* out, float* lse_out,
+                        int32_t* count_out, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return run_entry(DIFFKV_ENTRY_PREFILL, desc, q, k_cache, v_cache, block_table, seq_lens, q_lens,
+                   window, sinks, k_scale, v_scale, softmax_scale, out, lse_out, count_out,
+                   workspace, workspace_bytes, stream);
+}
+
+size_t diffkv_attn_workspace_bytes(const diffkv_attn_desc* desc, int entry) {
+  if (validate_desc(desc, entry) != DIFFKV_OK) return 0;
+  if (entry == DIFFKV_ENTRY_PREFILL) return 0;
+  return plan_split(*desc, 0, true).workspace_bytes;
+}
+
+int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry) {
+  return validate_desc(desc, entry);
+}
+
+int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window) {
+  if (validate_desc(desc, entry) != DIFFKV_OK) return 0;
+  if (entry == DIFFKV_ENTRY_PREFILL) return 1;
+  return plan_split(*desc, window, true).num_splits;
+}
+
+const char* diffkv_attn_strerror(int status) {
+  switch (status) {
+    case DIFFKV_OK: return "success";
+    case DIFFKV_INVALID_ARGUMENT: return "invalid argument";
+    case DIFFKV_UNSUPPORTED: return "unsupported shape, page size or dtype";
+    case DIFFKV_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DIFFKV_HIP_ERROR: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

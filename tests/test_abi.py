@@ -1,0 +1,121 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no compute call).
+
+The library must load, export every function include/diffkv_attn.h declares,
+and reject bad descriptors synchronously through diffkv_attn_validate.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_asymmetric_head_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "diffkv_attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(diffkv_attn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.library_path()):
+        pytest.fail("libdiffkv_attn.so is not built (run __graft_entry__.build())")
+    return B.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("diffkv_attn_decode", "diffkv_attn_verify", "diffkv_attn_prefill",
+              "diffkv_attn_workspace_bytes", "diffkv_attn_validate", "diffkv_attn_strerror",
+              "diffkv_attn_num_splits"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def good_desc(**kw):
+    d = dict(batch=4, num_q_heads=8, num_kv_heads=1, head_dim_qk=192, head_dim_v=128,
+             page_size=128, num_pages=2000, block_table_stride=400, max_seq_len=50000,
+             max_q_len=8, total_q=32, kv_dtype=B.KV_BF16, force_num_splits=0)
+    d.update(kw)
+    return B.AttnDesc(**d)
+
+
+def test_validate_accepts_good_descriptors(lib):
+    assert B.diffkv_attn_validate(good_desc(), B.ENTRY_VERIFY) == B.OK
+    assert B.diffkv_attn_validate(good_desc(), B.ENTRY_PREFILL) == B.OK
+    assert B.diffkv_attn_validate(good_desc(max_q_len=1, total_q=4), B.ENTRY_DECODE) == B.OK
+    assert B.diffkv_attn_validate(good_desc(kv_dtype=B.KV_FP8_E4M3, page_size=1,
+                                            block_table_stride=50000), B.ENTRY_VERIFY) == B.OK
+
+
+@pytest.mark.parametrize("field,value,entry,status", [
+    ("num_q_heads", 7, B.ENTRY_VERIFY, B.INVALID_ARGUMENT),       # Hq % Hkv with Hkv=2 below
+    ("head_dim_qk", 128, B.ENTRY_VERIFY, B.UNSUPPORTED),
+    ("head_dim_v", 192, B.ENTRY_VERIFY, B.UNSUPPORTED),
+    ("page_size", 96, B.ENTRY_VERIFY, B.UNSUPPORTED),
+    ("page_size", 512, B.ENTRY_VERIFY, B.UNSUPPORTED),
+    ("kv_dtype", 7, B.ENTRY_VERIFY, B.UNSUPPORTED),
+    ("batch", 0, B.ENTRY_VERIFY, B.INVALID_ARGUMENT),
+    ("max_q_len", 17, B.ENTRY_VERIFY, B.INVALID_ARGUMENT),
+    ("max_q_len", 8, B.ENTRY_DECODE, B.INVALID_ARGUMENT),
+    ("block_table_stride", 390, B.ENTRY_VERIFY, B.INVALID_ARGUMENT),
+    ("total_q", 33, B.ENTRY_VERIFY, B.INVALID_ARGUMENT),
+    ("total_q", 3, B.ENTRY_VERIFY, B.INVALID_ARGUMENT),
+    ("force_num_splits", -1, B.ENTRY_VERIFY, B.INVALID_ARGUMENT),
+    ("num_pages", 0, B.ENTRY_VERIFY, B.INVALID_ARGUMENT),
+])
+def test_validate_rejects(lib, field, value, entry, status):
+    kw = {field: value}
+    if field == "num_q_heads":
+        kw["num_kv_heads"] = 2
+    assert B.diffkv_attn_validate(good_desc(**kw), entry) == status
+
+
+def test_validate_rejects_null_and_bad_entry(lib):
+    assert lib.diffkv_attn_validate(None, 0) == B.INVALID_ARGUMENT
+    assert B.diffkv_attn_validate(good_desc(), 3) == B.INVALID_ARGUMENT
+
+
+def test_workspace_and_splits(lib):
+    d = good_desc()
+    ns = B.diffkv_attn_num_splits(d, B.ENTRY_VERIFY)
+    assert ns > 1
+    ws = B.diffkv_attn_workspace_bytes(d, B.ENTRY_VERIFY)
+    # partial rows (fp32 x 128) + one lse per row, per split, per 64-row query tile
+    assert ws >= 4 * 1 * ns * 64 * (128 + 1) * 4
+    assert B.diffkv_attn_workspace_bytes(d, B.ENTRY_PREFILL) == 0
+    assert B.diffkv_attn_num_splits(d, B.ENTRY_PREFILL) == 1
+    # A window only shrinks the split count, so the full-attention workspace covers it.
+    assert B.diffkv_attn_num_splits(d, B.ENTRY_VERIFY, 128) <= ns
+    # Forced split count.
+    assert B.diffkv_attn_num_splits(good_desc(force_num_splits=7), B.ENTRY_VERIFY) == 7
+    # Invalid descriptor -> 0 bytes.
+    assert B.diffkv_attn_workspace_bytes(good_desc(batch=0), B.ENTRY_VERIFY) == 0
+
+
+def test_strerror(lib):
+    assert B.diffkv_attn_strerror(B.OK) == "success"
+    assert "workspace" in B.diffkv_attn_strerror(B.WORKSPACE_TOO_SMALL)
+    assert B.diffkv_attn_strerror(99) == "unknown status"
+
+
+def test_entry_rejects_before_touching_the_gpu(lib):
+    """Argument errors return synchronously, before any HIP call."""
+    d = good_desc(head_dim_qk=64)
+    fn = lib.diffkv_attn_verify
+    st = fn(ctypes.byref(d), None, None, None, None, None, None, 0, None, 1.0, 1.0, 1.0,
+            None, None, None, None, 0, None)
+    assert st == B.UNSUPPORTED
+    d = good_desc()
+    st = fn(ctypes.byref(d), None, None, None, None, None, None, 0, None, 1.0, 1.0, 1.0,
+            None, None, None, None, 0, None)
+    assert st == B.INVALID_ARGUMENT
