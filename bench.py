@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Throughput of the paged asymmetric-head attention path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-extra] [--no-cpu-baseline]
+
+A step is one C-ABI call of the whole path (plan, block-table gather, FP8/bf16
+load, QK^T, mask, online softmax, PV, split partials and merge) over one batch
+of the seeded synthetic workload.  The headline workload is batched decode
+(32 sequences of 8192..9216 tokens, 8 query heads on 1 KV head, page 128,
+bf16 K/V); its metric is the KV bytes the visible keys occupy, read per
+second from HBM.
+
+The KV pool is replicated into enough copies ("layers") to exceed 1 GiB, and
+consecutive steps read consecutive copies, so no step finds its keys in the
+256 MB Infinity Cache or the L2.  Inputs are resident in HBM before timing.
+
+One JSON line is printed.  `roofline` is the main attention kernel alone:
+its duration comes from HIP events the library records around that kernel
+(diffkv_attn_profile_next_call), averaged over the timed steps.
+`cpu_baseline` times the FP64 oracle on the host on a bounded sample.
+`extra` carries the other workloads measured the same way.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KV-read HBM GB/s (decode/verify) + prefill TFLOP/s, each as % of MI355X peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+ENTRY_OF = {"tiny_decode": "decode", "batched_decode": "decode", "verify_long": "verify",
+            "swa_sinks_fp8_p1": "verify", "swa_sinks_fp8_p128": "verify",
+            "chunked_prefill": "prefill"}
+KERNEL_OF_ENTRY = {"decode": "split_attn_kernel", "verify": "split_attn_kernel",
+                   "prefill": "split_attn_kernel"}
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="batched_decode", choices=sorted(ENTRY_OF))
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--extra-steps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target host time for the oracle sample")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime's C API (raw pointers)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        for fn in ("hipEventCreate", "hipEventRecord", "hipEventSynchronize", "hipEventElapsedTime",
+                   "hipEventDestroy"):
+            getattr(self.lib, fn).restype = ctypes.c_int
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+
+def algorithmic_work(inp):
+    """Bytes of the KV rows the visible keys occupy (each read once per
+    (sequence, KV head)), (query row, visible key) pairs and their flops."""
+    import numpy as np
+    esize = 1 if inp.kv_dtype == "fp8" else 2
+    keys = 0
+    pairs = 0
+    qctx = 0
+    for b in range(inp.batch):
+        L, n = int(inp.seq_lens[b]), int(inp.q_lens[b])
+        p = L - n + np.arange(n)
+        lo = np.maximum(0, p - inp.window + 1) if inp.window > 0 else np.zeros_like(p)
+        keys += int(p.max() + 1 - lo.min())
+        vis = int((p - lo + 1).sum())
+        qctx += vis
+        pairs += vis * inp.num_q_heads
+    kv_bytes = keys * inp.num_kv_heads * (192 + 128) * esize
+    return {"kv_bytes": kv_bytes, "pairs": pairs, "flops": 640 * pairs, "q_ctx": qctx}
+
+
+def kernel_source_sha():
+    import glob
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "paged_asymmetric_head_amd", "csrc", "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, sha):
+    """HBM bytes per launch from the committed counter runs, if they were
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(workload)
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def measure(name, steps, warmup, events, target_bytes=1 << 30):
+    import torch
+    from paged_asymmetric_head_amd import binding as B
+    from paged_asymmetric_head_amd.device import DeviceInputs
+    from paged_asymmetric_head_amd.synth import workload
+
+    entry = ENTRY_OF[name]
+    inp = workload(name)
+    dev = DeviceInputs(inp)
+    pool = dev.k_cache.numel() * dev.k_cache.element_size() + dev.v_cache.numel() * dev.v_cache.element_size()
+    layers = max(1, min(16, math.ceil(target_bytes / pool)))
+    caches = [(dev.k_cache, dev.v_cache)] + [(dev.k_cache.clone(), dev.v_cache.clone())
+                                             for _ in range(layers - 1)]
+    stream = torch.cuda.current_stream().cuda_stream
+    calls = [dev.prepare(entry, k_cache=k, v_cache=v, stream=stream) for k, v in caches]
+    pairs = [(events.create(), events.create()) for _ in range(steps)]
+    t0, t1 = events.create(), events.create()
+
+    for i in range(warmup):
+        calls[i % layers]()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    events.record(t0, stream)
+    for k in range(steps):
+        B.diffkv_attn_profile_next_call(pairs[k][0], pairs[k][1])
+        calls[k % layers]()
+    events.record(t1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = events.elapsed_ms(t0, t1)
+    kern = sorted(events.elapsed_ms(a, b) for a, b in pairs)
+    out = calls[(steps - 1) % layers].out
+    if not bool(torch.isfinite(out.float()).all()):
+        raise RuntimeError(f"{name}: non-finite output")
+    work = algorithmic_work(inp)
+    d = dev.desc(entry)
+    splits = B.diffkv_attn_num_splits(d, B.ENTRIES[entry], inp.window)
+    return {
+        "inp": inp, "entry": entry, "layers": layers, "splits": splits,
+        "ms_per_step": total_ms / steps, "wall_ms_per_step": 1e3 * wall / steps,
+        "kernel_ms_mean": sum(kern) / len(kern), "kernel_ms_median": kern[len(kern) // 2],
+        "work": work,
+    }
+
+
+def roofline(m, sha, name):
+    w = m["work"]
+    ms = m["kernel_ms_mean"]
+    traffic = measured_traffic(name, sha)
+    if m["entry"] == "prefill":
+        achieved = w["flops"] / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": KERNEL_OF_ENTRY[m["entry"]],
+                "kernel_ms": round(ms, 5), "work_per_launch": w["flops"]}
+    achieved = w["kv_bytes"] / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": KERNEL_OF_ENTRY[m["entry"]], "kernel_ms": round(ms, 5),
+            "work_per_launch": w["kv_bytes"]}
+
+
+def summary(m, sha, name):
+    w = m["work"]
+    s = m["ms_per_step"] * 1e-3
+    res = {"entry": m["entry"], "ms_per_step": round(m["ms_per_step"], 5),
+           "kv_gbs": round(w["kv_bytes"] / s / 1e9, 1),
+           "tflops": round(w["flops"] / s / 1e12, 2),
+           "q_ctx_tokens_per_s": w["q_ctx"] / s, "splits": m["splits"], "layers": m["layers"],
+           "roofline": roofline(m, sha, name)}
+    return res
+
+
+def cpu_baseline(name, seconds):
+    """The FP64 oracle on the host: whole query tokens of the workload until
+    about `seconds` of work, rate scaled to the metric's unit."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import paged_attention
+    from paged_asymmetric_head_amd.synth import workload
+
+    inp = workload(name)
+    entry = ENTRY_OF[name]
+    args = inp.oracle_kwargs()
+    starts = np.concatenate([[0], np.cumsum(inp.q_lens)[:-1]])
+    order = np.random.default_rng(0).permutation(inp.batch)
+    done_bytes = done_flops = 0
+    n_tok = 0
+    t0 = time.perf_counter()
+    esize = 1 if inp.kv_dtype == "fp8" else 2
+    for b in order:
+        L, n = int(inp.seq_lens[b]), int(inp.q_lens[b])
+        chunk = n if entry != "prefill" else 8
+        for c0 in range(0, n, chunk):
+            toks = np.arange(starts[b] + c0, starts[b] + min(n, c0 + chunk))
+            paged_attention(**args, tokens=toks)
+            p = L - n + (toks - starts[b])
+            lo = np.maximum(0, p - inp.window + 1) if inp.window > 0 else np.zeros_like(p)
+            done_bytes += int(p.max() + 1 - lo.min()) * inp.num_kv_heads * 320 * esize
+            done_flops += 640 * int((p - lo + 1).sum()) * inp.num_q_heads
+            n_tok += len(toks)
+            if time.perf_counter() - t0 >= seconds:
+                break
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
+    if entry == "prefill":
+        val, unit = done_flops / dt / 1e12, "TFLOP/s"
+    else:
+        val, unit = done_bytes / dt / 1e9, "GB/s"
+    return {"value": round(val, 6), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{name}: {n_tok} of {inp.total_q} query tokens, all heads, in {dt:.1f} s "
+                      f"(FP64 NumPy oracle, BLAS threads={threads})"}
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this attention path has no cross-GPU step; "
+              "run it with --gpus 1 (see the sharding design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    from paged_asymmetric_head_amd import binding as B
+    B.load_library()
+    sha = kernel_source_sha()
+    events = HipEvents()
+
+    name = args.workload
+    print(f"[bench] {name}: generating and measuring", file=sys.stderr, flush=True)
+    m = measure(name, args.steps, args.warmup, events)
+    head = summary(m, sha, name)
+    inp = m["inp"]
+    is_prefill = m["entry"] == "prefill"
+    value = head["tflops"] if is_prefill else head["kv_gbs"]
+    result = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s" if is_prefill else "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "entry": m["entry"], "batch": inp.batch,
+                   "q_len": int(inp.q_lens.max()), "context_max": int(inp.max_seq_len),
+                   "num_q_heads": inp.num_q_heads, "num_kv_heads": inp.num_kv_heads,
+                   "head_dim_qk": 192, "head_dim_v": 128, "page_size": inp.page_size,
+                   "kv_dtype": inp.kv_dtype, "window": inp.window,
+                   "sinks": inp.sinks is not None, "splits": m["splits"], "kv_copies": m["layers"],
+                   "kv_bytes_per_step": m["work"]["kv_bytes"]},
+        "q_ctx_tokens_per_s": head["q_ctx_tokens_per_s"],
+        "wall_ms_per_step": round(m["wall_ms_per_step"], 5),
+        "roofline": head["roofline"],
+        "kernel_source_sha": sha,
+    }
+    del m
+    if not args.no_extra:
+        extra = {}
+        for other in ("verify_long", "swa_sinks_fp8_p1", "swa_sinks_fp8_p128", "chunked_prefill"):
+            if other == name:
+                continue
+            print(f"[bench] {other}: generating and measuring", file=sys.stderr, flush=True)
+            mo = measure(other, args.extra_steps, 5, events)
+            extra[other] = summary(mo, sha, other)
+            del mo
+            torch.cuda.empty_cache()
+        result["extra"] = extra
+    if not args.no_cpu_baseline:
+        print(f"[bench] {name}: timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

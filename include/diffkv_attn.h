@@ -161,6 +161,15 @@ int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry);
  * window (1 for prefill; 0 for an invalid descriptor).  Host only. */
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window);
 
+/* Profiling hook.  Arms two caller-created HIP events for the next
+ * decode/verify/prefill call made on this host thread: that call records
+ * `start` on its stream just before its main attention kernel and `stop`
+ * just after it (before the split merge), so hipEventElapsedTime(start,
+ * stop) is that kernel's duration.  The hook disarms after one call; passing
+ * two NULLs disarms it.  Returns DIFFKV_INVALID_ARGUMENT if exactly one event
+ * is NULL. */
+int diffkv_attn_profile_next_call(hipEvent_t start, hipEvent_t stop);
+
 /* Static text for a status code. */
 const char* diffkv_attn_strerror(int status);
 

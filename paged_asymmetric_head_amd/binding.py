@@ -58,6 +58,8 @@ def load_library():
     lib.diffkv_attn_validate.restype = ctypes.c_int
     lib.diffkv_attn_num_splits.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int, ctypes.c_int32]
     lib.diffkv_attn_num_splits.restype = ctypes.c_int
+    lib.diffkv_attn_profile_next_call.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.diffkv_attn_profile_next_call.restype = ctypes.c_int
     lib.diffkv_attn_strerror.argtypes = [ctypes.c_int]
     lib.diffkv_attn_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -96,6 +98,34 @@ def diffkv_attn_workspace_bytes(desc, entry):
 
 def diffkv_attn_num_splits(desc, entry, window=0):
     return int(load_library().diffkv_attn_num_splits(ctypes.byref(desc), int(entry), int(window)))
+
+
+def diffkv_attn_profile_next_call(start, stop):
+    """Arm two raw hipEvent_t handles (ints) around the next call's main kernel."""
+    status = load_library().diffkv_attn_profile_next_call(start, stop)
+    if status != OK:
+        raise DiffKVError(f"diffkv_attn_profile_next_call: {diffkv_attn_strerror(status)}")
+
+
+def prepared_call(name, desc, q, k_cache, v_cache, block_table, seq_lens, q_lens, window, sinks,
+                  k_scale, v_scale, softmax_scale, out, lse_out=None, count_out=None,
+                  workspace=None, workspace_bytes=0, stream=None):
+    """Resolve every argument once and return a no-argument callable that
+    makes the C-ABI call (for tight timing loops); it raises on a bad status."""
+    fn = getattr(load_library(), name)
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(seq_lens), _ptr(q_lens), int(window), _ptr(sinks), float(k_scale),
+            float(v_scale), float(softmax_scale), _ptr(out), _ptr(lse_out), _ptr(count_out),
+            _ptr(workspace), int(workspace_bytes), _stream(stream))
+    keep = (desc, q, k_cache, v_cache, block_table, seq_lens, q_lens, sinks, out, lse_out,
+            count_out, workspace)
+
+    def call():
+        status = fn(*args)
+        if status != OK:
+            raise DiffKVError(f"{name}: {diffkv_attn_strerror(status)} (status {status})")
+    call.keep_alive = keep
+    return call
 
 
 def _call(name, desc, q, k_cache, v_cache, block_table, seq_lens, q_lens, window, sinks,

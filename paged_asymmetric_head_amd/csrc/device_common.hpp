@@ -32,6 +32,16 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of
+// 16 lanes the four 16-bit values each lane reads are concatenated in lane
+// order into S[0..64); lane i of the group receives S[i], S[16+i], S[32+i],
+// S[48+i].
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // fp32 -> bf16, round to nearest even (hardware conversion on gfx950).

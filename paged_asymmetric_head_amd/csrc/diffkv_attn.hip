@@ -16,6 +16,10 @@ using namespace diffkv;
 
 namespace {
 
+// Events armed by diffkv_attn_profile_next_call for this thread's next call.
+thread_local hipEvent_t g_profile_start = nullptr;
+thread_local hipEvent_t g_profile_stop = nullptr;
+
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int ilog2(int x) {
@@ -51,28 +55,38 @@ int validate_desc(const diffkv_attn_desc* d, int entry) {
   return DIFFKV_OK;
 }
 
-template <bool FP8, int RT, bool DIRECT, bool COUNT>
+template <bool FP8, int RT, bool DIRECT, bool COUNT, bool UPAGE>
 hipError_t launch_split_kernel(const SplitArgs& a, dim3 grid, hipStream_t stream) {
   void* args[] = {const_cast<SplitArgs*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&split_attn_kernel<FP8, RT, DIRECT, COUNT>),
-                         grid, dim3(256), args, 0, stream);
+  constexpr int NS = kSplitStages<FP8>;
+  return hipLaunchKernel(
+      reinterpret_cast<const void*>(&split_attn_kernel<FP8, RT, DIRECT, COUNT, UPAGE, NS>), grid,
+      dim3(256), args, 0, stream);
 }
 
-template <bool FP8, int RT>
+template <bool FP8, int RT, bool UPAGE>
 hipError_t dispatch_split_rt(const SplitArgs& a, dim3 grid, bool direct, bool count, hipStream_t st) {
-  if (direct) return count ? launch_split_kernel<FP8, RT, true, true>(a, grid, st)
-                           : launch_split_kernel<FP8, RT, true, false>(a, grid, st);
-  return count ? launch_split_kernel<FP8, RT, false, true>(a, grid, st)
-               : launch_split_kernel<FP8, RT, false, false>(a, grid, st);
+  if (direct) return count ? launch_split_kernel<FP8, RT, true, true, UPAGE>(a, grid, st)
+                           : launch_split_kernel<FP8, RT, true, false, UPAGE>(a, grid, st);
+  return count ? launch_split_kernel<FP8, RT, false, true, UPAGE>(a, grid, st)
+               : launch_split_kernel<FP8, RT, false, false, UPAGE>(a, grid, st);
 }
 
+// UPAGE: pages of at least one 64-key tile, so a tile never straddles pages.
 template <bool FP8>
-hipError_t dispatch_split(const SplitArgs& a, int rt, dim3 grid, bool direct, bool count,
-                          hipStream_t st) {
+hipError_t dispatch_split(const SplitArgs& a, int rt, bool upage, dim3 grid, bool direct,
+                          bool count, hipStream_t st) {
+  if (upage) {
+    switch (rt) {
+      case 1: return dispatch_split_rt<FP8, 1, true>(a, grid, direct, count, st);
+      case 2: return dispatch_split_rt<FP8, 2, true>(a, grid, direct, count, st);
+      default: return dispatch_split_rt<FP8, 4, true>(a, grid, direct, count, st);
+    }
+  }
   switch (rt) {
-    case 1: return dispatch_split_rt<FP8, 1>(a, grid, direct, count, st);
-    case 2: return dispatch_split_rt<FP8, 2>(a, grid, direct, count, st);
-    default: return dispatch_split_rt<FP8, 4>(a, grid, direct, count, st);
+    case 1: return dispatch_split_rt<FP8, 1, false>(a, grid, direct, count, st);
+    case 2: return dispatch_split_rt<FP8, 2, false>(a, grid, direct, count, st);
+    default: return dispatch_split_rt<FP8, 4, false>(a, grid, direct, count, st);
   }
 }
 
@@ -81,7 +95,7 @@ hipError_t launch_merge(const SplitArgs& a, int rows, dim3 grid, hipStream_t str
   const void* fn = rows == 16 ? reinterpret_cast<const void*>(&split_merge_kernel<16>)
                  : rows == 32 ? reinterpret_cast<const void*>(&split_merge_kernel<32>)
                               : reinterpret_cast<const void*>(&split_merge_kernel<64>);
-  return hipLaunchKernel(fn, grid, dim3(64), args, 0, stream);
+  return hipLaunchKernel(fn, grid, dim3(256), args, 0, stream);
 }
 
 hipError_t launch_fill(int32_t* p, size_t n, hipStream_t stream) {
@@ -116,7 +130,8 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
   }
 
   // Prefill runs one split per query tile (its many query rows fill the GPU).
-  const SplitPlan plan = plan_split(*d, window, entry != DIFFKV_ENTRY_PREFILL);
+  const SplitPlan plan = plan_split(*d, window, entry != DIFFKV_ENTRY_PREFILL,
+                                    split_wgs_per_cu(fp8, d->page_size >= kTileKeys));
   if (plan.num_splits > 1 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
     return DIFFKV_WORKSPACE_TOO_SMALL;
 
@@ -149,8 +164,14 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
 
   const dim3 grid(plan.num_splits, plan.n_qtiles, d->batch * d->num_kv_heads);
   const bool direct = plan.num_splits == 1;
-  hipError_t e = fp8 ? dispatch_split<true>(a, plan.row_tiles, grid, direct, count_out != nullptr, stream)
-                     : dispatch_split<false>(a, plan.row_tiles, grid, direct, count_out != nullptr, stream);
+  const bool upage = d->page_size >= kTileKeys;
+  hipEvent_t ev_start = g_profile_start, ev_stop = g_profile_stop;
+  g_profile_start = g_profile_stop = nullptr;
+  hipError_t e = ev_start ? hipEventRecord(ev_start, stream) : hipSuccess;
+  if (e == hipSuccess)
+    e = fp8 ? dispatch_split<true>(a, plan.row_tiles, upage, grid, direct, count_out != nullptr, stream)
+            : dispatch_split<false>(a, plan.row_tiles, upage, grid, direct, count_out != nullptr, stream);
+  if (e == hipSuccess && ev_stop) e = hipEventRecord(ev_stop, stream);
   if (e == hipSuccess && !direct)
     e = launch_merge(a, plan.rows, dim3(plan.n_qtiles * plan.rows, d->batch * d->num_kv_heads), stream);
   return e == hipSuccess ? DIFFKV_OK : DIFFKV_HIP_ERROR;
@@ -206,7 +227,16 @@ int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry) {
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window) {
   if (validate_desc(desc, entry) != DIFFKV_OK) return 0;
   if (entry == DIFFKV_ENTRY_PREFILL) return 1;
-  return plan_split(*desc, window, true).num_splits;
+  return plan_split(*desc, window, true,
+                    split_wgs_per_cu(desc->kv_dtype == DIFFKV_KV_FP8_E4M3, desc->page_size >= kTileKeys))
+      .num_splits;
+}
+
+int diffkv_attn_profile_next_call(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr)) return DIFFKV_INVALID_ARGUMENT;
+  g_profile_start = start;
+  g_profile_stop = stop;
+  return DIFFKV_OK;
 }
 
 const char* diffkv_attn_strerror(int status) {

@@ -44,14 +44,38 @@ inline long long max_keys_bound(const diffkv_attn_desc& d, int window) {
   return full;
 }
 
-// Split count: enough workgroups to cover the 256 CUs about twice, but never
-// fewer than `kMinTilesPerSplit` tiles per split (the split partials are
-// extra traffic, so short splits do not pay).  Monotone in the key bound, so
-// the workspace sized for full attention covers every window.
-constexpr int kWaveTargetWGs = 2 * kTargetCUs;
+// Register stages of the split kernel (tiles of K/V in flight per
+// workgroup) and the workgroups that stay resident per CU with them
+// (bf16 stages are twice as large, so fewer workgroups fit).
+// Register stages of the split kernel (tiles of K/V in flight per
+// workgroup) and the waves per SIMD it is compiled for.  With pages of at
+// least one tile the block-table lookups are scalar and two workgroups fit a
+// CU; smaller pages keep per-lane page ids and fit one.
+#ifndef DIFFKV_BF16_STAGES
+#define DIFFKV_BF16_STAGES 2
+#endif
+#ifndef DIFFKV_FP8_STAGES
+#define DIFFKV_FP8_STAGES 4
+#endif
+#ifndef DIFFKV_UPAGE_WAVES_PER_EU
+#define DIFFKV_UPAGE_WAVES_PER_EU 2
+#endif
+template <bool FP8> constexpr int kSplitStages = FP8 ? DIFFKV_FP8_STAGES : DIFFKV_BF16_STAGES;
+constexpr int split_waves_per_eu(bool /*fp8*/, bool upage) {
+  return upage ? DIFFKV_UPAGE_WAVES_PER_EU : 1;
+}
+inline int split_wgs_per_cu(bool fp8, bool upage) { return split_waves_per_eu(fp8, upage); }
+
+// Split count: one resident round of workgroups over the 256 CUs (a second
+// round would pay the start-up chain seq_lens -> block table -> data again),
+// but never fewer than `kMinTilesPerSplit` tiles per split (the split
+// partials are extra traffic, so short splits do not pay).  Monotone in the
+// key bound, so the workspace sized for full attention covers every window;
+// the workspace is sized for the largest target (4 workgroups per CU).
 constexpr int kMinTilesPerSplit = 4;
 
-inline SplitPlan plan_split(const diffkv_attn_desc& d, int window, bool allow_split) {
+inline SplitPlan plan_split(const diffkv_attn_desc& d, int window, bool allow_split,
+                            int wgs_per_cu = 4) {
   SplitPlan p;
   const int G = d.num_q_heads / d.num_kv_heads;
   const long long rows_pair = (long long)d.max_q_len * G;
@@ -65,7 +89,8 @@ inline SplitPlan plan_split(const diffkv_attn_desc& d, int window, bool allow_sp
     if (d.force_num_splits > 0) {
       s = d.force_num_splits;
     } else {
-      long long want = (kWaveTargetWGs + pairs - 1) / pairs;
+      const long long target = (long long)kTargetCUs * wgs_per_cu;
+      long long want = (target + pairs - 1) / pairs;
       long long cap = tiles / kMinTilesPerSplit;
       if (cap < 1) cap = 1;
       if (want > cap) want = cap;

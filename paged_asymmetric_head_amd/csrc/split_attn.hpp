@@ -20,7 +20,8 @@
 //   O^T += V^T * P^T     (v_mfma_f32_16x16x16_bf16, 8 tiles over 128 dims)
 // Keeping S and O transposed puts one query row in each lane, so the softmax
 // rescale needs no data movement between lanes.
-// The next tile's global loads are issued before the current tile's math.
+// The global loads of the next NS tiles are in flight in registers while a
+// tile is converted into LDS and multiplied.
 #pragma once
 
 #include "device_common.hpp"
@@ -29,9 +30,14 @@
 namespace diffkv {
 
 constexpr int kKLdsStride = kHeadDimQK + 8;   // bf16 per K row in LDS (400 B, conflict-free reads)
-constexpr int kVtLdsStride = kTileKeys + 4;    // bf16 per V^T row in LDS (136 B)
+constexpr int kVLdsStride = kHeadDimV + 16;   // bf16 per V row in LDS (288 B: the 16 rows of
+                                               // a transposing read fall in distinct bank windows)
 constexpr int kKLdsElems = kTileKeys * kKLdsStride;
-constexpr int kVtLdsElems = kHeadDimV * kVtLdsStride;
+constexpr int kVLdsElems = kTileKeys * kVLdsStride;
+
+// Sixteen zero bytes (static device memory is zero-filled at load): the
+// source of every load whose key lies outside the range a tile may read.
+__device__ __attribute__((aligned(16))) uint8_t g_zero_row[16];
 
 struct SplitArgs {
   const uint16_t* q;
@@ -75,8 +81,9 @@ __device__ __forceinline__ void split_tiles(int kv_lo, int kv_hi, int S, int s, 
   n_valid = (nt + tps - 1) / tps;
 }
 
-template <bool FP8, int RT, bool DIRECT, bool COUNT>
-__global__ __launch_bounds__(256) void split_attn_kernel(const SplitArgs a) {
+template <bool FP8, int RT, bool DIRECT, bool COUNT, bool UPAGE, int NS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(split_waves_per_eu(FP8, UPAGE), 8)))
+void split_attn_kernel(const SplitArgs a) {
   constexpr int ROWS = 16 * RT;
   constexpr int KW = 4 / RT;                 // waves splitting the keys of one row tile
   constexpr int SUBS = kTileKeys / 16 / KW;  // 16-key subtiles per wave per tile
@@ -85,11 +92,13 @@ __global__ __launch_bounds__(256) void split_attn_kernel(const SplitArgs a) {
   constexpr int V_UPR = kHeadDimV * ESZ / 16;
   constexpr int KU = kTileKeys * K_UPR / 256;    // units per thread per tile
   constexpr int VU = kTileKeys * V_UPR / 256;
+  constexpr int NPK = UPAGE ? 1 : KU;            // page ids held per thread per tile
+  constexpr int NPV = UPAGE ? 1 : VU;
   static_assert(kTileKeys * K_UPR % 256 == 0 && kTileKeys * V_UPR % 256 == 0, "tile split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kKLdsElems + kVtLdsElems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kKLdsElems + kVLdsElems];
   uint16_t* k_lds = lds;
-  uint16_t* vt_lds = lds + kKLdsElems;
+  uint16_t* v_lds = lds + kKLdsElems;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -106,6 +115,112 @@ __global__ __launch_bounds__(256) void split_attn_kernel(const SplitArgs a) {
   qtile_key_range(L, n, G, qt, ROWS, a.window, kv_lo, kv_hi);
   split_tiles(kv_lo, kv_hi, a.num_splits, s, t_begin, t_end, n_valid);
   if (t_begin >= t_end) return;
+
+  const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
+  const int lp = a.log2_page;
+  const int pmask = (1 << lp) - 1;
+  const size_t k_row_bytes = (size_t)kHeadDimQK * ESZ, v_row_bytes = (size_t)kHeadDimV * ESZ;
+
+  // Fixed unit -> (row, piece) maps: consecutive lanes take consecutive
+  // 16-byte pieces of a row, so every wave load covers whole rows.
+  auto k_row = [&](int k) { return (tid + 256 * k) / K_UPR; };
+  auto k_piece = [&](int k) { return (tid + 256 * k) % K_UPR; };
+  auto v_key = [&](int k) { return (tid + 256 * k) / V_UPR; };
+  auto v_piece = [&](int k) { return (tid + 256 * k) % V_UPR; };
+
+  struct Pages { int k[NPK]; int v[NPV]; };
+  struct Stage { u32x4 k[KU]; u32x4 v[VU]; };
+
+  // Physical page ids of tile t.  Every load below is unconditional (a
+  // branch around a load makes the compiler wait for all loads in flight):
+  // tiles past the split re-read the split's last tile and keys outside the
+  // union range read a static zero row instead of their page.
+  auto fetch_pages = [&](int t, Pages& p) {
+    const int tc = min(t, t_end - 1);
+    if constexpr (UPAGE) {
+      p.k[0] = bt[(tc * kTileKeys) >> lp];
+      p.v[0] = p.k[0];
+    } else {
+#pragma unroll
+      for (int k = 0; k < KU; ++k) {
+        const int j = tc * kTileKeys + k_row(k);
+        p.k[k] = bt[((j >= kv_lo && j < kv_hi) ? j : kv_lo) >> lp];
+      }
+#pragma unroll
+      for (int k = 0; k < VU; ++k) {
+        const int j = tc * kTileKeys + v_key(k);
+        p.v[k] = bt[((j >= kv_lo && j < kv_hi) ? j : kv_lo) >> lp];
+      }
+    }
+  };
+
+  // Gather tile t's K and V rows into registers.
+  auto fetch_data = [&](int t, const Pages& p, Stage& st) {
+    const int tc = min(t, t_end - 1);
+#pragma unroll
+    for (int k = 0; k < KU; ++k) {
+      const int j = tc * kTileKeys + k_row(k);
+      const int pg = UPAGE ? p.k[0] : p.k[k];
+      const size_t slot = ((size_t)pg << lp) | (size_t)(j & pmask);
+      const uint8_t* src = (j >= kv_lo && j < kv_hi)
+                               ? a.k_cache + (slot * a.hkv + g) * k_row_bytes + k_piece(k) * 16
+                               : g_zero_row;
+      st.k[k] = *reinterpret_cast<const u32x4*>(src);
+    }
+#pragma unroll
+    for (int k = 0; k < VU; ++k) {
+      const int j = tc * kTileKeys + v_key(k);
+      const int pg = UPAGE ? p.v[0] : p.v[k];
+      const size_t slot = ((size_t)pg << lp) | (size_t)(j & pmask);
+      const uint8_t* src = (j >= kv_lo && j < kv_hi)
+                               ? a.v_cache + (slot * a.hkv + g) * v_row_bytes + v_piece(k) * 16
+                               : g_zero_row;
+      st.v[k] = *reinterpret_cast<const u32x4*>(src);
+    }
+  };
+
+  // Registers -> LDS as bf16, both row-major (FP8 widened on the way).
+  auto store_tile = [&](const Stage& st) {
+#pragma unroll
+    for (int k = 0; k < KU; ++k) {
+      const int row = k_row(k), piece = k_piece(k);
+      if constexpr (FP8) {
+        const u32x2 c0 = e4m3x4_to_bf16x4(st.k[k].x), c1 = e4m3x4_to_bf16x4(st.k[k].y);
+        const u32x2 c2 = e4m3x4_to_bf16x4(st.k[k].z), c3 = e4m3x4_to_bf16x4(st.k[k].w);
+        u32x4* dst = reinterpret_cast<u32x4*>(k_lds + row * kKLdsStride + piece * 16);
+        dst[0] = u32x4{c0.x, c0.y, c1.x, c1.y};
+        dst[1] = u32x4{c2.x, c2.y, c3.x, c3.y};
+      } else {
+        *reinterpret_cast<u32x4*>(k_lds + row * kKLdsStride + piece * 8) = st.k[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < VU; ++k) {
+      const int key = v_key(k), piece = v_piece(k);
+      if constexpr (FP8) {
+        const u32x2 c0 = e4m3x4_to_bf16x4(st.v[k].x), c1 = e4m3x4_to_bf16x4(st.v[k].y);
+        const u32x2 c2 = e4m3x4_to_bf16x4(st.v[k].z), c3 = e4m3x4_to_bf16x4(st.v[k].w);
+        u32x4* dst = reinterpret_cast<u32x4*>(v_lds + key * kVLdsStride + piece * 16);
+        dst[0] = u32x4{c0.x, c0.y, c1.x, c1.y};
+        dst[1] = u32x4{c2.x, c2.y, c3.x, c3.y};
+      } else {
+        *reinterpret_cast<u32x4*>(v_lds + key * kVLdsStride + piece * 8) = st.v[k];
+      }
+    }
+  };
+
+  // NS tiles of K/V in flight in registers; page ids NS tiles ahead of the
+  // data they address.
+  Pages pg[NS];
+  Stage st[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) fetch_pages(t_begin + i, pg[i]);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    fetch_data(t_begin + i, pg[i], st[i]);
+    fetch_pages(t_begin + NS + i, pg[i]);
+  }
+
   const int r0 = seq_row_start(a.q_lens, b);
 
   // The query row this lane owns in S^T / O^T.
@@ -123,7 +238,8 @@ __global__ __launch_bounds__(256) void split_attn_kernel(const SplitArgs a) {
     const uint16_t* qp = a.q + ((size_t)(r0 + tok) * a.hq + h) * kHeadDimQK + 8 * grp;
 #pragma unroll
     for (int c = 0; c < 6; ++c)
-      qreg[c] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 32 * c) : u32x4{0, 0, 0, 0};
+      qreg[c] = *reinterpret_cast<const u32x4*>(row_ok ? reinterpret_cast<const uint8_t*>(qp + 32 * c)
+                                                       : g_zero_row);
   }
 
   float m = -INFINITY, l = 0.f;
@@ -132,133 +248,83 @@ __global__ __launch_bounds__(256) void split_attn_kernel(const SplitArgs a) {
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   int cnt = 0;
 
-  const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
-  const int pmask = (1 << a.log2_page) - 1;
-  const size_t k_row_bytes = (size_t)kHeadDimQK * ESZ, v_row_bytes = (size_t)kHeadDimV * ESZ;
-  u32x4 kbuf[KU], vbuf[VU];
-
-  // Gather one tile's K and V rows into registers; keys outside the union
-  // range are never touched (their pages may be unmapped) and read as zero.
-  auto load_tile = [&](int t) {
-    const int base = t * kTileKeys;
+  // One online-softmax update per tile: the S^T tiles of all this wave's
+  // 16-key subtiles first (independent MFMA chains), one max / rescale / sum
+  // over them, then all the P*V products.
+  auto compute_tile = [&](int t) {
+    f32x4 sacc[SUBS];
 #pragma unroll
-    for (int k = 0; k < KU; ++k) {
-      const int u = tid + 256 * k;
-      const int row = u / K_UPR, piece = u % K_UPR;
-      const int j = base + row;
-      kbuf[k] = u32x4{0, 0, 0, 0};
-      if (j >= kv_lo && j < kv_hi) {
-        const size_t slot = ((size_t)bt[j >> a.log2_page] << a.log2_page) | (size_t)(j & pmask);
-        kbuf[k] = *reinterpret_cast<const u32x4*>(a.k_cache + (slot * a.hkv + g) * k_row_bytes + piece * 16);
+    for (int sub = 0; sub < SUBS; ++sub) sacc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 6; ++c)
+#pragma unroll
+      for (int sub = 0; sub < SUBS; ++sub) {
+        const uint16_t* kp = k_lds + ((kg * SUBS + sub) * 16 + col) * kKLdsStride + 8 * grp + 32 * c;
+        sacc[sub] = mfma_16x16x32(*reinterpret_cast<const u32x4*>(kp), qreg[c], sacc[sub]);
       }
-    }
-#pragma unroll
-    for (int k = 0; k < VU; ++k) {
-      const int u = tid + 256 * k;
-      const int row = u / V_UPR, piece = u % V_UPR;
-      const int j = base + row;
-      vbuf[k] = u32x4{0, 0, 0, 0};
-      if (j >= kv_lo && j < kv_hi) {
-        const size_t slot = ((size_t)bt[j >> a.log2_page] << a.log2_page) | (size_t)(j & pmask);
-        vbuf[k] = *reinterpret_cast<const u32x4*>(a.v_cache + (slot * a.hkv + g) * v_row_bytes + piece * 16);
-      }
-    }
-  };
 
-  // Registers -> LDS as bf16: K row-major, V transposed (dims x keys).
-  auto store_tile = [&]() {
+    // sacc[sub][i] = S^T[key (kg*SUBS+sub)*16 + 4*grp + i][row col].  Masked by select only.
+    float x[SUBS][4];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < KU; ++k) {
-      const int u = tid + 256 * k;
-      const int row = u / K_UPR, piece = u % K_UPR;
-      if constexpr (FP8) {
-        const u32x2 c0 = e4m3x4_to_bf16x4(kbuf[k].x), c1 = e4m3x4_to_bf16x4(kbuf[k].y);
-        const u32x2 c2 = e4m3x4_to_bf16x4(kbuf[k].z), c3 = e4m3x4_to_bf16x4(kbuf[k].w);
-        u32x4* dst = reinterpret_cast<u32x4*>(k_lds + row * kKLdsStride + piece * 16);
-        dst[0] = u32x4{c0.x, c0.y, c1.x, c1.y};
-        dst[1] = u32x4{c2.x, c2.y, c3.x, c3.y};
-      } else {
-        *reinterpret_cast<u32x4*>(k_lds + row * kKLdsStride + piece * 8) = kbuf[k];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < VU; ++k) {
-      const int u = tid + 256 * k;
-      const int row = u / V_UPR, piece = u % V_UPR;
-      if constexpr (FP8) {
-        const u32x2 c[4] = {e4m3x4_to_bf16x4(vbuf[k].x), e4m3x4_to_bf16x4(vbuf[k].y),
-                            e4m3x4_to_bf16x4(vbuf[k].z), e4m3x4_to_bf16x4(vbuf[k].w)};
-        uint16_t* dst = vt_lds + (piece * 16) * kVtLdsStride + row;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dst[(4 * e + 0) * kVtLdsStride] = (uint16_t)(c[e].x & 0xffff);
-          dst[(4 * e + 1) * kVtLdsStride] = (uint16_t)(c[e].x >> 16);
-          dst[(4 * e + 2) * kVtLdsStride] = (uint16_t)(c[e].y & 0xffff);
-          dst[(4 * e + 3) * kVtLdsStride] = (uint16_t)(c[e].y >> 16);
-        }
-      } else {
-        const uint32_t w[4] = {vbuf[k].x, vbuf[k].y, vbuf[k].z, vbuf[k].w};
-        uint16_t* dst = vt_lds + (piece * 8) * kVtLdsStride + row;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dst[(2 * e + 0) * kVtLdsStride] = (uint16_t)(w[e] & 0xffff);
-          dst[(2 * e + 1) * kVtLdsStride] = (uint16_t)(w[e] >> 16);
-        }
-      }
-    }
-  };
-
-  load_tile(t_begin);
-  for (int t = t_begin; t < t_end; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < t_end) load_tile(t + 1);
-
-#pragma unroll
-    for (int sub = 0; sub < SUBS; ++sub) {
-      const int kb = (kg * SUBS + sub) * 16;
-      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kp = k_lds + (kb + col) * kKLdsStride + 8 * grp;
-#pragma unroll
-      for (int c = 0; c < 6; ++c)
-        sacc = mfma_16x16x32(*reinterpret_cast<const u32x4*>(kp + 32 * c), qreg[c], sacc);
-
-      // sacc[i] = S^T[key kb + 4*grp + i][row col].  Masked by select only.
-      const int j0 = t * kTileKeys + kb + 4 * grp;
-      float x[4];
-      float mx = -INFINITY;
+    for (int sub = 0; sub < SUBS; ++sub)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = j0 + i;
+        const int j = t * kTileKeys + (kg * SUBS + sub) * 16 + 4 * grp + i;
         const bool vis = j >= lo_row && j <= hi_row;
-        x[i] = vis ? sacc[i] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, x[i]);
+        x[sub][i] = vis ? sacc[sub][i] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[sub][i]);
         if constexpr (COUNT) cnt += vis ? 1 : 0;
       }
-      mx = wave_max_xor(mx, 16);
-      mx = wave_max_xor(mx, 32);
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      float pr[4], ps = 0.f;
+    mx = wave_max_xor(mx, 16);
+    mx = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    float ps = 0.f;
+    u32x2 pb[SUBS];
+#pragma unroll
+    for (int sub = 0; sub < SUBS; ++sub) {
+      float pr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pr[i] = fast_exp2(x[i] - m_use);
+        pr[i] = fast_exp2(x[sub][i] - m_use);
         ps += pr[i];
       }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
-      l = l * alpha + ps;
-      m = m_new;
+      pb[sub] = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * alpha + ps;
+    m = m_new;
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn) o[nn] *= alpha;
+    for (int nn = 0; nn < 8; ++nn) o[nn] *= alpha;
 
-      const u32x2 pb = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
-      const uint16_t* vp = vt_lds + col * kVtLdsStride + kb + 4 * grp;
+    // V^T operand straight from the row-major tile: in each 16-lane group the
+    // transposing read hands lane col the dim 16*nn + col of keys
+    // 4*grp + 0..3 when source lane col reads 4 dims (16*nn + 4*(col%4))
+    // of key 4*grp + col/4.
+#pragma unroll
+    for (int sub = 0; sub < SUBS; ++sub) {
+      const uint16_t* vp = v_lds + ((kg * SUBS + sub) * 16 + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
 #pragma unroll
       for (int nn = 0; nn < 8; ++nn)
-        o[nn] = mfma_16x16x16(*reinterpret_cast<const u32x2*>(vp + nn * 16 * kVtLdsStride), pb, o[nn]);
+        o[nn] = mfma_16x16x16(lds_read_tr16(vp + 16 * nn), pb[sub], o[nn]);
+    }
+  };
+
+  // Every stage step runs in every round (loads stay in one fixed order, so
+  // the compiler waits for exactly the stage it needs); only the math of
+  // tiles past the split is skipped.
+  for (int t = t_begin; t < t_end; t += NS) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      __syncthreads();
+      store_tile(st[i]);
+      __syncthreads();
+      fetch_data(t + i + NS, pg[i], st[i]);
+      fetch_pages(t + i + 2 * NS, pg[i]);
+      if (t + i < t_end) compute_tile(t + i);
     }
   }
 
@@ -272,7 +338,7 @@ __global__ __launch_bounds__(256) void split_attn_kernel(const SplitArgs a) {
   // Waves that split the keys of one row tile combine through LDS.
   if constexpr (KW > 1) {
     constexpr int STR = 34;
-    static_assert(4 * 64 * STR * 4 <= (kKLdsElems + kVtLdsElems) * 2, "reduction fits");
+    static_assert(4 * 64 * STR * 4 <= (kKLdsElems + kVLdsElems) * 2, "reduction fits");
     __syncthreads();
     float* red = reinterpret_cast<float*>(lds);
     float* mine = red + (wave * 64 + lane) * STR;
@@ -335,12 +401,27 @@ __global__ __launch_bounds__(256) void split_attn_kernel(const SplitArgs a) {
   }
 }
 
+__device__ __forceinline__ float wave_max_all(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_all(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
 // Combines the split partials of one query row: weights 2^(lse_s - M), the
-// sink joining the denominator, v_scale, bf16 store.  One wave per row, two
-// output dims per lane.  Splits are read in a fixed order (deterministic).
+// sink joining the denominator, v_scale, bf16 store.  One 256-thread
+// workgroup per row.  Lanes read 64 splits' lse values at a time; wave w
+// then takes splits w, w+4, ... of that group with all sixteen of its
+// partial-row loads (two output dims per lane) in flight together, and the
+// four partial sums meet in LDS in a fixed order (deterministic).
 template <int ROWS>
-__global__ __launch_bounds__(64) void split_merge_kernel(const SplitArgs a) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void split_merge_kernel(const SplitArgs a) {
+  __shared__ f32x2 red[3][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int qt = blockIdx.x / ROWS, r = blockIdx.x % ROWS;
   const int bg = blockIdx.y;
   const int b = bg / a.hkv, g = bg % a.hkv;
@@ -352,22 +433,45 @@ __global__ __launch_bounds__(64) void split_merge_kernel(const SplitArgs a) {
   int kv_lo, kv_hi, t_begin, t_end, n_valid;
   qtile_key_range(L, n, G, qt, ROWS, a.window, kv_lo, kv_hi);
   split_tiles(kv_lo, kv_hi, a.num_splits, 0, t_begin, t_end, n_valid);
-  const int r0 = seq_row_start(a.q_lens, b);
   const int tok = R / G, h = g * G + R % G;
+  const float s2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
 
   const size_t prow0 = ((size_t)bg * a.n_qtiles + qt) * a.num_splits * ROWS + r;
+  // Pass over groups of 64 splits; the common case (<= 64 splits) is one pass.
   float M = -INFINITY;
-  for (int s = 0; s < n_valid; ++s) M = fmaxf(M, a.part_lse[prow0 + (size_t)s * ROWS]);
-  const float s2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
+  for (int s0 = 0; s0 < n_valid; s0 += 64)
+    if (s0 + lane < n_valid) M = fmaxf(M, a.part_lse[prow0 + (size_t)(s0 + lane) * ROWS]);
+  M = wave_max_all(M);
   const float Mt = fmaxf(M, s2);
+
   f32x2 acc = f32x2{0.f, 0.f};
   float ksum = 0.f;
-  for (int s = 0; s < n_valid; ++s) {
-    const size_t pr = prow0 + (size_t)s * ROWS;
-    const float w = fast_exp2(a.part_lse[pr] - Mt);
-    ksum += w;
-    acc += w * *reinterpret_cast<const f32x2*>(a.part_o + pr * kHeadDimV + 2 * lane);
+  for (int s0 = 0; s0 < n_valid; s0 += 64) {
+    const int sl = s0 + lane;
+    const float wl = sl < n_valid ? fast_exp2(a.part_lse[prow0 + (size_t)sl * ROWS] - Mt) : 0.f;
+    ksum += wl;
+    const float* po = a.part_o + (prow0 + (size_t)s0 * ROWS) * kHeadDimV + 2 * lane;
+    f32x2 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int i = min(wave + 4 * k, 63);
+      v[k] = *reinterpret_cast<const f32x2*>(po + (size_t)min(i, n_valid - 1 - s0) * ROWS * kHeadDimV);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int i = wave + 4 * k;
+      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), min(i, 63)));
+      if (s0 + i < n_valid) acc += w * v[k];
+    }
   }
+  if (wave > 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave > 0) return;
+  acc += red[0][lane];
+  acc += red[1][lane];
+  acc += red[2][lane];
+  ksum = wave_sum_all(ksum);
+  const int r0 = seq_row_start(a.q_lens, b);
   const float den = ksum + (a.sinks ? fast_exp2(s2 - Mt) : 0.f);
   const float coef = a.v_scale / den;
   const size_t out_row = (size_t)(r0 + tok) * a.hq + h;

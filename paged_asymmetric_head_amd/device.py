@@ -75,3 +75,25 @@ class DeviceInputs:
            self.sinks if isinstance(sinks, str) else sinks, inp.k_scale, inp.v_scale,
            inp.softmax_scale, out, lse_t, cnt_t, ws, nbytes, stream)
         return out, lse_t, cnt_t
+
+    def prepare(self, entry, *, k_cache=None, v_cache=None, force_num_splits=0, stream=None,
+                lse=False, count=False):
+        """Allocate outputs and workspace once and return a no-argument callable
+        making one C-ABI call (its `.out` is the output tensor)."""
+        inp = self.inp
+        d = self.desc(entry, force_num_splits)
+        out = torch.empty((inp.total_q, inp.num_q_heads, inp.v_cache.shape[3]),
+                          dtype=torch.bfloat16, device=self.device)
+        lse_t = torch.empty((inp.total_q, inp.num_q_heads), dtype=torch.float32,
+                            device=self.device) if lse else None
+        cnt_t = torch.empty((inp.total_q, inp.num_q_heads), dtype=torch.int32,
+                            device=self.device) if count else None
+        ws, nbytes = self.workspace_for(entry, force_num_splits)
+        call = B.prepared_call(f"diffkv_attn_{entry}", d, self.q,
+                               self.k_cache if k_cache is None else k_cache,
+                               self.v_cache if v_cache is None else v_cache,
+                               self.block_table, self.seq_lens, self.q_lens, inp.window,
+                               self.sinks, inp.k_scale, inp.v_scale, inp.softmax_scale, out,
+                               lse_t, cnt_t, ws, nbytes, stream)
+        call.out, call.lse, call.count = out, lse_t, cnt_t
+        return call
