@@ -52,16 +52,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Four OCP E4M3FN codes (one 32-bit word, byte 0 first) -> four bf16 codes in
-// two words.  The hardware converter yields the exact fp32 value (NaN codes
-// give NaN); every finite E4M3 value has at most 4 significant bits and an
-// exponent in [-9, 8], so dropping the low 16 bits of the fp32 is exact.
+// two words, with gfx950's packed converter at scale 1.0.  Every finite
+// E4M3 value has at most 4 significant bits and an exponent in [-9, 8], so
+// it is exact in bf16; NaN codes give NaN.
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
-  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  u32x2 r;
-  r.x = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u);
-  r.y = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u);
-  return r;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true);
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

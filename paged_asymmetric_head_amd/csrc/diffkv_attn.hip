@@ -11,6 +11,7 @@
 #include "diffkv_attn.h"
 #include "plan.hpp"
 #include "split_attn.hpp"
+#include "prefill_attn.hpp"
 
 using namespace diffkv;
 
@@ -47,8 +48,8 @@ int validate_desc(const diffkv_attn_desc* d, int entry) {
   if (entry == DIFFKV_ENTRY_VERIFY && d->max_q_len > 16) return DIFFKV_INVALID_ARGUMENT;
   // Launch-shape limits.
   if ((long long)d->batch * d->num_kv_heads > kMaxGridYZ) return DIFFKV_UNSUPPORTED;
-  {
-    const SplitPlan p = plan_split(*d, 0, entry != DIFFKV_ENTRY_PREFILL);
+  if (entry != DIFFKV_ENTRY_PREFILL) {
+    const SplitPlan p = plan_split(*d, 0, true);
     if (p.n_qtiles > kMaxGridYZ) return DIFFKV_UNSUPPORTED;
   }
   if ((long long)d->total_q * d->num_q_heads > (1LL << 31) / kHeadDimQK) return DIFFKV_UNSUPPORTED;
@@ -98,6 +99,21 @@ hipError_t launch_merge(const SplitArgs& a, int rows, dim3 grid, hipStream_t str
   return hipLaunchKernel(fn, grid, dim3(256), args, 0, stream);
 }
 
+template <bool FP8, bool UPAGE, bool COUNT>
+hipError_t launch_prefill_kernel(const SplitArgs& a, dim3 grid, hipStream_t stream) {
+  void* args[] = {const_cast<SplitArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&prefill_attn_kernel<FP8, UPAGE, COUNT>),
+                         grid, dim3(256), args, 0, stream);
+}
+
+template <bool FP8>
+hipError_t dispatch_prefill(const SplitArgs& a, bool upage, bool count, dim3 grid, hipStream_t st) {
+  if (upage) return count ? launch_prefill_kernel<FP8, true, true>(a, grid, st)
+                          : launch_prefill_kernel<FP8, true, false>(a, grid, st);
+  return count ? launch_prefill_kernel<FP8, false, true>(a, grid, st)
+               : launch_prefill_kernel<FP8, false, false>(a, grid, st);
+}
+
 hipError_t launch_fill(int32_t* p, size_t n, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   int32_t zero = 0;
@@ -116,12 +132,12 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
   if (st != DIFFKV_OK) return st;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return DIFFKV_INVALID_ARGUMENT;
   if (!q_lens && d->max_q_len != 1) return DIFFKV_INVALID_ARGUMENT;
-  if (!std::isfinite(softmax_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
-    return DIFFKV_INVALID_ARGUMENT;
-
   const bool fp8 = d->kv_dtype == DIFFKV_KV_FP8_E4M3;
   const float ks = fp8 ? k_scale : 1.f;
   const float vs = fp8 ? v_scale : 1.f;
+  if (!std::isfinite(softmax_scale) || !std::isfinite(ks) || !std::isfinite(vs) ||
+      !(softmax_scale > 0.f) || !(ks > 0.f))
+    return DIFFKV_INVALID_ARGUMENT;
   const int G = d->num_q_heads / d->num_kv_heads;
 
   if (count_out) {
@@ -129,9 +145,43 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
     if (e != hipSuccess) return DIFFKV_HIP_ERROR;
   }
 
-  // Prefill runs one split per query tile (its many query rows fill the GPU).
-  const SplitPlan plan = plan_split(*d, window, entry != DIFFKV_ENTRY_PREFILL,
-                                    split_wgs_per_cu(fp8, d->page_size >= kTileKeys));
+  const bool upage = d->page_size >= kTileKeys;
+  if (entry == DIFFKV_ENTRY_PREFILL) {
+    // One workgroup per 128 query rows of a (sequence, KV head); the many
+    // rows of a chunk fill the GPU without splitting the keys.
+    SplitArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint8_t*>(k_cache);
+    a.v_cache = static_cast<const uint8_t*>(v_cache);
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.q_lens = q_lens;
+    a.sinks = sinks;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse_out = lse_out;
+    a.count_out = count_out;
+    a.hq = d->num_q_heads;
+    a.hkv = d->num_kv_heads;
+    a.group = G;
+    a.log2_page = ilog2(d->page_size);
+    a.bt_stride = d->block_table_stride;
+    a.window = window;
+    a.n_qtiles = prefill_row_blocks(*d);
+    a.num_splits = 1;
+    a.scale_log2 = softmax_scale * ks * kLog2e;
+    a.v_scale = vs;
+    const dim3 grid(a.n_qtiles, d->batch * d->num_kv_heads);
+    hipEvent_t ev_start = g_profile_start, ev_stop = g_profile_stop;
+    g_profile_start = g_profile_stop = nullptr;
+    hipError_t e = ev_start ? hipEventRecord(ev_start, stream) : hipSuccess;
+    if (e == hipSuccess)
+      e = fp8 ? dispatch_prefill<true>(a, upage, count_out != nullptr, grid, stream)
+              : dispatch_prefill<false>(a, upage, count_out != nullptr, grid, stream);
+    if (e == hipSuccess && ev_stop) e = hipEventRecord(ev_stop, stream);
+    return e == hipSuccess ? DIFFKV_OK : DIFFKV_HIP_ERROR;
+  }
+
+  const SplitPlan plan = plan_split(*d, window, true, split_wgs_per_cu(fp8, upage));
   if (plan.num_splits > 1 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
     return DIFFKV_WORKSPACE_TOO_SMALL;
 
@@ -164,7 +214,6 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
 
   const dim3 grid(plan.num_splits, plan.n_qtiles, d->batch * d->num_kv_heads);
   const bool direct = plan.num_splits == 1;
-  const bool upage = d->page_size >= kTileKeys;
   hipEvent_t ev_start = g_profile_start, ev_stop = g_profile_stop;
   g_profile_start = g_profile_stop = nullptr;
   hipError_t e = ev_start ? hipEventRecord(ev_start, stream) : hipSuccess;

@@ -24,20 +24,9 @@
 // tile is converted into LDS and multiplied.
 #pragma once
 
-#include "device_common.hpp"
-#include "plan.hpp"
+#include "kv_tile.hpp"
 
 namespace diffkv {
-
-constexpr int kKLdsStride = kHeadDimQK + 8;   // bf16 per K row in LDS (400 B, conflict-free reads)
-constexpr int kVLdsStride = kHeadDimV + 16;   // bf16 per V row in LDS (288 B: the 16 rows of
-                                               // a transposing read fall in distinct bank windows)
-constexpr int kKLdsElems = kTileKeys * kKLdsStride;
-constexpr int kVLdsElems = kTileKeys * kVLdsStride;
-
-// Sixteen zero bytes (static device memory is zero-filled at load): the
-// source of every load whose key lies outside the range a tile may read.
-__device__ __attribute__((aligned(16))) uint8_t g_zero_row[16];
 
 struct SplitArgs {
   const uint16_t* q;
@@ -58,17 +47,6 @@ struct SplitArgs {
   float v_scale;      // v_scale for FP8 caches, 1 for bf16
 };
 
-// Keys one query tile can see: the union of its rows' ranges.
-__device__ __forceinline__ void qtile_key_range(int L, int n, int G, int qt, int rows, int window,
-                                                int& kv_lo, int& kv_hi) {
-  const int r_lo = qt * rows;
-  const int r_hi = min(n * G, r_lo + rows) - 1;
-  const int p_lo = L - n + r_lo / G;
-  const int p_hi = L - n + r_hi / G;
-  kv_lo = window > 0 ? max(0, p_lo - window + 1) : 0;
-  kv_hi = p_hi + 1;
-}
-
 // Tiles of split s among S equal shares of the aligned tile range.
 __device__ __forceinline__ void split_tiles(int kv_lo, int kv_hi, int S, int s, int& t_begin,
                                             int& t_end, int& n_valid) {
@@ -87,15 +65,7 @@ void split_attn_kernel(const SplitArgs a) {
   constexpr int ROWS = 16 * RT;
   constexpr int KW = 4 / RT;                 // waves splitting the keys of one row tile
   constexpr int SUBS = kTileKeys / 16 / KW;  // 16-key subtiles per wave per tile
-  constexpr int ESZ = FP8 ? 1 : 2;
-  constexpr int K_UPR = kHeadDimQK * ESZ / 16;   // 16-byte units per K row
-  constexpr int V_UPR = kHeadDimV * ESZ / 16;
-  constexpr int KU = kTileKeys * K_UPR / 256;    // units per thread per tile
-  constexpr int VU = kTileKeys * V_UPR / 256;
-  constexpr int NPK = UPAGE ? 1 : KU;            // page ids held per thread per tile
-  constexpr int NPV = UPAGE ? 1 : VU;
-  static_assert(kTileKeys * K_UPR % 256 == 0 && kTileKeys * V_UPR % 256 == 0, "tile split");
-
+  using IO = KvTile<FP8, UPAGE>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kKLdsElems + kVLdsElems];
   uint16_t* k_lds = lds;
   uint16_t* v_lds = lds + kKLdsElems;
@@ -116,109 +86,19 @@ void split_attn_kernel(const SplitArgs a) {
   split_tiles(kv_lo, kv_hi, a.num_splits, s, t_begin, t_end, n_valid);
   if (t_begin >= t_end) return;
 
-  const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
-  const int lp = a.log2_page;
-  const int pmask = (1 << lp) - 1;
-  const size_t k_row_bytes = (size_t)kHeadDimQK * ESZ, v_row_bytes = (size_t)kHeadDimV * ESZ;
-
-  // Fixed unit -> (row, piece) maps: consecutive lanes take consecutive
-  // 16-byte pieces of a row, so every wave load covers whole rows.
-  auto k_row = [&](int k) { return (tid + 256 * k) / K_UPR; };
-  auto k_piece = [&](int k) { return (tid + 256 * k) % K_UPR; };
-  auto v_key = [&](int k) { return (tid + 256 * k) / V_UPR; };
-  auto v_piece = [&](int k) { return (tid + 256 * k) % V_UPR; };
-
-  struct Pages { int k[NPK]; int v[NPV]; };
-  struct Stage { u32x4 k[KU]; u32x4 v[VU]; };
-
-  // Physical page ids of tile t.  Every load below is unconditional (a
-  // branch around a load makes the compiler wait for all loads in flight):
-  // tiles past the split re-read the split's last tile and keys outside the
-  // union range read a static zero row instead of their page.
-  auto fetch_pages = [&](int t, Pages& p) {
-    const int tc = min(t, t_end - 1);
-    if constexpr (UPAGE) {
-      p.k[0] = bt[(tc * kTileKeys) >> lp];
-      p.v[0] = p.k[0];
-    } else {
-#pragma unroll
-      for (int k = 0; k < KU; ++k) {
-        const int j = tc * kTileKeys + k_row(k);
-        p.k[k] = bt[((j >= kv_lo && j < kv_hi) ? j : kv_lo) >> lp];
-      }
-#pragma unroll
-      for (int k = 0; k < VU; ++k) {
-        const int j = tc * kTileKeys + v_key(k);
-        p.v[k] = bt[((j >= kv_lo && j < kv_hi) ? j : kv_lo) >> lp];
-      }
-    }
-  };
-
-  // Gather tile t's K and V rows into registers.
-  auto fetch_data = [&](int t, const Pages& p, Stage& st) {
-    const int tc = min(t, t_end - 1);
-#pragma unroll
-    for (int k = 0; k < KU; ++k) {
-      const int j = tc * kTileKeys + k_row(k);
-      const int pg = UPAGE ? p.k[0] : p.k[k];
-      const size_t slot = ((size_t)pg << lp) | (size_t)(j & pmask);
-      const uint8_t* src = (j >= kv_lo && j < kv_hi)
-                               ? a.k_cache + (slot * a.hkv + g) * k_row_bytes + k_piece(k) * 16
-                               : g_zero_row;
-      st.k[k] = *reinterpret_cast<const u32x4*>(src);
-    }
-#pragma unroll
-    for (int k = 0; k < VU; ++k) {
-      const int j = tc * kTileKeys + v_key(k);
-      const int pg = UPAGE ? p.v[0] : p.v[k];
-      const size_t slot = ((size_t)pg << lp) | (size_t)(j & pmask);
-      const uint8_t* src = (j >= kv_lo && j < kv_hi)
-                               ? a.v_cache + (slot * a.hkv + g) * v_row_bytes + v_piece(k) * 16
-                               : g_zero_row;
-      st.v[k] = *reinterpret_cast<const u32x4*>(src);
-    }
-  };
-
-  // Registers -> LDS as bf16, both row-major (FP8 widened on the way).
-  auto store_tile = [&](const Stage& st) {
-#pragma unroll
-    for (int k = 0; k < KU; ++k) {
-      const int row = k_row(k), piece = k_piece(k);
-      if constexpr (FP8) {
-        const u32x2 c0 = e4m3x4_to_bf16x4(st.k[k].x), c1 = e4m3x4_to_bf16x4(st.k[k].y);
-        const u32x2 c2 = e4m3x4_to_bf16x4(st.k[k].z), c3 = e4m3x4_to_bf16x4(st.k[k].w);
-        u32x4* dst = reinterpret_cast<u32x4*>(k_lds + row * kKLdsStride + piece * 16);
-        dst[0] = u32x4{c0.x, c0.y, c1.x, c1.y};
-        dst[1] = u32x4{c2.x, c2.y, c3.x, c3.y};
-      } else {
-        *reinterpret_cast<u32x4*>(k_lds + row * kKLdsStride + piece * 8) = st.k[k];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < VU; ++k) {
-      const int key = v_key(k), piece = v_piece(k);
-      if constexpr (FP8) {
-        const u32x2 c0 = e4m3x4_to_bf16x4(st.v[k].x), c1 = e4m3x4_to_bf16x4(st.v[k].y);
-        const u32x2 c2 = e4m3x4_to_bf16x4(st.v[k].z), c3 = e4m3x4_to_bf16x4(st.v[k].w);
-        u32x4* dst = reinterpret_cast<u32x4*>(v_lds + key * kVLdsStride + piece * 16);
-        dst[0] = u32x4{c0.x, c0.y, c1.x, c1.y};
-        dst[1] = u32x4{c2.x, c2.y, c3.x, c3.y};
-      } else {
-        *reinterpret_cast<u32x4*>(v_lds + key * kVLdsStride + piece * 8) = st.v[k];
-      }
-    }
-  };
+  const IO io(a.k_cache, a.v_cache, a.block_table + (size_t)b * a.bt_stride, a.hkv, g,
+              a.log2_page, kv_lo, kv_hi, t_end, tid);
 
   // NS tiles of K/V in flight in registers; page ids NS tiles ahead of the
   // data they address.
-  Pages pg[NS];
-  Stage st[NS];
+  typename IO::Pages pg[NS];
+  typename IO::Stage st[NS];
 #pragma unroll
-  for (int i = 0; i < NS; ++i) fetch_pages(t_begin + i, pg[i]);
+  for (int i = 0; i < NS; ++i) io.fetch_pages(t_begin + i, pg[i]);
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    fetch_data(t_begin + i, pg[i], st[i]);
-    fetch_pages(t_begin + NS + i, pg[i]);
+    io.fetch_data(t_begin + i, pg[i], st[i]);
+    io.fetch_pages(t_begin + NS + i, pg[i]);
   }
 
   const int r0 = seq_row_start(a.q_lens, b);
@@ -320,10 +200,10 @@ void split_attn_kernel(const SplitArgs a) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       __syncthreads();
-      store_tile(st[i]);
+      io.store(st[i], k_lds, v_lds);
       __syncthreads();
-      fetch_data(t + i + NS, pg[i], st[i]);
-      fetch_pages(t + i + 2 * NS, pg[i]);
+      io.fetch_data(t + i + NS, pg[i], st[i]);
+      io.fetch_pages(t + i + 2 * NS, pg[i]);
       if (t + i < t_end) compute_tile(t + i);
     }
   }

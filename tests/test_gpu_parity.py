@@ -125,3 +125,29 @@ def test_run_to_run_bitwise_determinism_and_page_permutation():
     c, _, _ = dev.run("verify", block_table=bt2)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+@pytest.mark.parametrize("entry", ["verify", "prefill"])
+def test_fp8_values_pass_through_exactly(entry):
+    """Window 1: each token sees only its own key, so out = V_p * v_scale.  With
+    v_scale 1 and V rows holding every finite E4M3 code, the output must be
+    the decoded codes bit for bit (each is exact in bf16)."""
+    from oracle import decode_e4m3fn
+    inp = make_paged_inputs(91, seq_lens=[9], q_lens=8, num_q_heads=2, num_kv_heads=1,
+                            page_size=4, kv_dtype="fp8", window=1, write_align=4)
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]
+    L, n = 9, 8
+    rows = np.resize(codes, (n, 128))
+    for i in range(n):
+        pos = L - n + i
+        inp.v_cache[inp.block_table[0, pos // 4], pos % 4, 0, :] = rows[i]
+    inp.v_scale = 1.0
+    dev = DeviceInputs(inp)
+    say(f"fp8 pass-through via {entry}")
+    out, _, _ = dev.run(entry)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    want = decode_e4m3fn(rows)
+    for h in range(2):
+        assert np.array_equal(got[:, h, :], want), "E4M3 decode is not exact on the GPU"
