@@ -41,7 +41,7 @@ ENTRY_OF = {"tiny_decode": "decode", "batched_decode": "decode", "verify_long": 
             "swa_sinks_fp8_p1": "verify", "swa_sinks_fp8_p128": "verify",
             "chunked_prefill": "prefill"}
 KERNEL_OF_ENTRY = {"decode": "split_attn_kernel", "verify": "split_attn_kernel",
-                   "prefill": "split_attn_kernel"}
+                   "prefill": "prefill_attn_kernel"}
 
 
 def parse_args():
@@ -55,6 +55,12 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target host time for the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reads and writes 256 MiB), the "
+                         "reference the HBM byte counters are scaled by")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--copy-calibration run into profiles/hbm_traffic.json and exit")
     return ap.parse_args()
 
 
@@ -173,6 +179,65 @@ def measure(name, steps, warmup, events, target_bytes=1 << 30):
     }
 
 
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration():
+    """A plain elementwise copy of known size: reads and writes COPY_BYTES."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+
+
+def _counter_means(path, counter):
+    """Mean per-dispatch value of one counter, by kernel name (rocprofv3 CSV)."""
+    import csv
+    import collections
+    per = collections.defaultdict(float)
+    names = {}
+    for row in csv.DictReader(open(path)):
+        if row["Counter_Name"] != counter:
+            continue
+        per[row["Dispatch_Id"]] += float(row["Counter_Value"])
+        names[row["Dispatch_Id"]] = row["Kernel_Name"]
+    by_kernel = collections.defaultdict(list)
+    for d, v in per.items():
+        by_kernel[names[d]].append(v)
+    return {k: sum(v) / len(v) for k, v in by_kernel.items()}
+
+
+def write_traffic(workload, fetch_csv, write_csv):
+    """HBM bytes per launch of the main kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the counter reads for the
+    calibration copy (COPY_BYTES read and written)."""
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    kern = KERNEL_OF_ENTRY[ENTRY_OF[workload]]
+
+    def pick(d, key):
+        hits = [v for k, v in d.items() if key in k]
+        if not hits:
+            raise SystemExit(f"no dispatch of {key} in the counter file")
+        return max(hits)
+
+    copy_key = "AUnaryFunctor<float, float, float"   # torch.mul(src, 1.0, out=dst)
+    f_factor = COPY_BYTES / (pick(fetch, copy_key) * 1024.0)
+    w_factor = COPY_BYTES / (pick(write, copy_key) * 1024.0)
+    rec = {"kernel": kern, "source_sha": kernel_source_sha(),
+           "fetch_kib_raw": pick(fetch, kern), "write_kib_raw": pick(write, kern),
+           "copy_fetch_factor": f_factor, "copy_write_factor": w_factor}
+    rec["bytes_per_launch"] = int(rec["fetch_kib_raw"] * 1024 * f_factor + rec["write_kib_raw"] * 1024 * w_factor)
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[workload] = rec
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps({workload: rec}))
+
+
 def roofline(m, sha, name):
     w = m["work"]
     ms = m["kernel_ms_mean"]
@@ -246,6 +311,9 @@ def cpu_baseline(name, seconds):
 
 def main():
     args = parse_args()
+    if args.traffic_from:
+        write_traffic(args.workload, *args.traffic_from)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this attention path has no cross-GPU step; "
@@ -296,6 +364,8 @@ def main():
             del mo
             torch.cuda.empty_cache()
         result["extra"] = extra
+    if args.copy_calibration:
+        copy_calibration()
     if not args.no_cpu_baseline:
         print(f"[bench] {name}: timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)

@@ -162,12 +162,12 @@ int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry);
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window);
 
 /* Profiling hook.  Arms two caller-created HIP events for the next
- * decode/verify/prefill call made on this host thread: that call records
- * `start` on its stream just before its main attention kernel and `stop`
- * just after it (before the split merge), so hipEventElapsedTime(start,
- * stop) is that kernel's duration.  The hook disarms after one call; passing
- * two NULLs disarms it.  Returns DIFFKV_INVALID_ARGUMENT if exactly one event
- * is NULL. */
+ * decode/verify/prefill call made on this host thread: that call's main
+ * attention kernel (not the split merge) is dispatched with them as its
+ * start and stop events (hipExtLaunchKernel), so hipEventElapsedTime(start,
+ * stop) is that kernel's execution time.  The hook disarms after one call;
+ * passing two NULLs disarms it.  Returns DIFFKV_INVALID_ARGUMENT if exactly
+ * one event is NULL. */
 int diffkv_attn_profile_next_call(hipEvent_t start, hipEvent_t stop);
 
 /* Static text for a status code. */

@@ -32,6 +32,9 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
+// Four bf16 ones, an MFMA operand that sums the other operand's columns.
+constexpr u32x2 kOnesBf16x4 = u32x2{0x3F803F80u, 0x3F803F80u};
+
 // gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of
 // 16 lanes the four 16-bit values each lane reads are concatenated in lane
 // order into S[0..64); lane i of the group receives S[i], S[16+i], S[32+i],
@@ -44,11 +47,11 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// fp32 -> bf16, round to nearest even (hardware conversion on gfx950).
+// Two fp32 -> two bf16 in one word, round to nearest even (one
+// v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo);
-  __bf16 b = static_cast<__bf16>(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Four OCP E4M3FN codes (one 32-bit word, byte 0 first) -> four bf16 codes in

@@ -5,6 +5,7 @@
 // it derives every launch from the descriptor, so calls can be captured in a
 // HIP graph.  Errors are status codes; no exception crosses the ABI.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cmath>
 
@@ -56,13 +57,24 @@ int validate_desc(const diffkv_attn_desc* d, int entry) {
   return DIFFKV_OK;
 }
 
+// Launches the main attention kernel of a call.  When profiling events are
+// armed, the dispatch itself stamps them (hipExtLaunchKernel), so their
+// elapsed time is the kernel's execution alone.
+hipError_t launch_main(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream) {
+  hipEvent_t start = g_profile_start, stop = g_profile_stop;
+  g_profile_start = g_profile_stop = nullptr;
+  if (start != nullptr)
+    return hipExtLaunchKernel(fn, grid, block, args, 0, stream, start, stop, 0);
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
 template <bool FP8, int RT, bool DIRECT, bool COUNT, bool UPAGE>
 hipError_t launch_split_kernel(const SplitArgs& a, dim3 grid, hipStream_t stream) {
   void* args[] = {const_cast<SplitArgs*>(&a)};
   constexpr int NS = kSplitStages<FP8>;
-  return hipLaunchKernel(
+  return launch_main(
       reinterpret_cast<const void*>(&split_attn_kernel<FP8, RT, DIRECT, COUNT, UPAGE, NS>), grid,
-      dim3(256), args, 0, stream);
+      dim3(256), args, stream);
 }
 
 template <bool FP8, int RT, bool UPAGE>
@@ -102,8 +114,8 @@ hipError_t launch_merge(const SplitArgs& a, int rows, dim3 grid, hipStream_t str
 template <bool FP8, bool UPAGE, bool COUNT>
 hipError_t launch_prefill_kernel(const SplitArgs& a, dim3 grid, hipStream_t stream) {
   void* args[] = {const_cast<SplitArgs*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&prefill_attn_kernel<FP8, UPAGE, COUNT>),
-                         grid, dim3(256), args, 0, stream);
+  return launch_main(reinterpret_cast<const void*>(&prefill_attn_kernel<FP8, UPAGE, COUNT>), grid,
+                     dim3(kPfThreads), args, stream);
 }
 
 template <bool FP8>
@@ -171,13 +183,8 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
     a.scale_log2 = softmax_scale * ks * kLog2e;
     a.v_scale = vs;
     const dim3 grid(a.n_qtiles, d->batch * d->num_kv_heads);
-    hipEvent_t ev_start = g_profile_start, ev_stop = g_profile_stop;
-    g_profile_start = g_profile_stop = nullptr;
-    hipError_t e = ev_start ? hipEventRecord(ev_start, stream) : hipSuccess;
-    if (e == hipSuccess)
-      e = fp8 ? dispatch_prefill<true>(a, upage, count_out != nullptr, grid, stream)
-              : dispatch_prefill<false>(a, upage, count_out != nullptr, grid, stream);
-    if (e == hipSuccess && ev_stop) e = hipEventRecord(ev_stop, stream);
+    const hipError_t e = fp8 ? dispatch_prefill<true>(a, upage, count_out != nullptr, grid, stream)
+                             : dispatch_prefill<false>(a, upage, count_out != nullptr, grid, stream);
     return e == hipSuccess ? DIFFKV_OK : DIFFKV_HIP_ERROR;
   }
 
@@ -214,13 +221,9 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
 
   const dim3 grid(plan.num_splits, plan.n_qtiles, d->batch * d->num_kv_heads);
   const bool direct = plan.num_splits == 1;
-  hipEvent_t ev_start = g_profile_start, ev_stop = g_profile_stop;
-  g_profile_start = g_profile_stop = nullptr;
-  hipError_t e = ev_start ? hipEventRecord(ev_start, stream) : hipSuccess;
-  if (e == hipSuccess)
-    e = fp8 ? dispatch_split<true>(a, plan.row_tiles, upage, grid, direct, count_out != nullptr, stream)
-            : dispatch_split<false>(a, plan.row_tiles, upage, grid, direct, count_out != nullptr, stream);
-  if (e == hipSuccess && ev_stop) e = hipEventRecord(ev_stop, stream);
+  hipError_t e =
+      fp8 ? dispatch_split<true>(a, plan.row_tiles, upage, grid, direct, count_out != nullptr, stream)
+          : dispatch_split<false>(a, plan.row_tiles, upage, grid, direct, count_out != nullptr, stream);
   if (e == hipSuccess && !direct)
     e = launch_merge(a, plan.rows, dim3(plan.n_qtiles * plan.rows, d->batch * d->num_kv_heads), stream);
   return e == hipSuccess ? DIFFKV_OK : DIFFKV_HIP_ERROR;

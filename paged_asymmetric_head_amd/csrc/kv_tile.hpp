@@ -7,7 +7,9 @@
 // FP8KV-W4A8-2x-RTX-PRO-6000", What the kernels do).  A workgroup of 256
 // threads moves a tile as 16-byte units, consecutive lanes on consecutive
 // pieces of a row, through registers: the caller keeps several tiles' loads
-// in flight (`Stage`s) and writes the oldest into LDS.
+// in flight (`Stage`s) and writes the oldest into LDS.  NT threads share a
+// tile (256 or 512); when they do not divide it evenly, whole waves take one
+// unit fewer.
 #pragma once
 
 #include "device_common.hpp"
@@ -25,16 +27,22 @@ constexpr int kVLdsElems = kTileKeys * kVLdsStride;
 // source of every load whose key lies outside the range a tile may read.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[16];
 
-template <bool FP8, bool UPAGE>
+template <bool FP8, bool UPAGE, int NT = 256>
 struct KvTile {
   static constexpr int ESZ = FP8 ? 1 : 2;
   static constexpr int K_UPR = kHeadDimQK * ESZ / 16;   // 16-byte units per K row
   static constexpr int V_UPR = kHeadDimV * ESZ / 16;
-  static constexpr int KU = kTileKeys * K_UPR / 256;    // units per thread per tile
-  static constexpr int VU = kTileKeys * V_UPR / 256;
+  static constexpr int K_UNITS = kTileKeys * K_UPR;     // units per tile
+  static constexpr int V_UNITS = kTileKeys * V_UPR;
+  static constexpr int KU = (K_UNITS + NT - 1) / NT;    // units per thread per tile
+  static constexpr int VU = (V_UNITS + NT - 1) / NT;
   static constexpr int NPK = UPAGE ? 1 : KU;            // page ids held per thread per tile
   static constexpr int NPV = UPAGE ? 1 : VU;
-  static_assert(kTileKeys * K_UPR % 256 == 0 && kTileKeys * V_UPR % 256 == 0, "tile split");
+  // A thread's last unit may not exist when NT does not divide the tile;
+  // the split is by whole waves (units come in multiples of 64).
+  static_assert(K_UNITS % 64 == 0 && V_UNITS % 64 == 0 && NT % 64 == 0, "wave-uniform split");
+  __device__ __forceinline__ bool k_has(int k) const { return tid + NT * k < K_UNITS; }
+  __device__ __forceinline__ bool v_has(int k) const { return tid + NT * k < V_UNITS; }
 
   struct Pages { int k[NPK]; int v[NPV]; };
   struct Stage { u32x4 k[KU]; u32x4 v[VU]; };
@@ -66,10 +74,11 @@ struct KvTile {
     }
   }
 
-  __device__ __forceinline__ int k_row(int k) const { return (tid + 256 * k) / K_UPR; }
-  __device__ __forceinline__ int k_piece(int k) const { return (tid + 256 * k) % K_UPR; }
-  __device__ __forceinline__ int v_key(int k) const { return (tid + 256 * k) / V_UPR; }
-  __device__ __forceinline__ int v_piece(int k) const { return (tid + 256 * k) % V_UPR; }
+  // Units past the tile (k_has false) map to row 0 and read the zero row.
+  __device__ __forceinline__ int k_row(int k) const { return k_has(k) ? (tid + NT * k) / K_UPR : 0; }
+  __device__ __forceinline__ int k_piece(int k) const { return (tid + NT * k) % K_UPR; }
+  __device__ __forceinline__ int v_key(int k) const { return v_has(k) ? (tid + NT * k) / V_UPR : 0; }
+  __device__ __forceinline__ int v_piece(int k) const { return (tid + NT * k) % V_UPR; }
   __device__ __forceinline__ bool readable(int j) const { return j >= kv_lo && j < kv_hi; }
 
   // Physical page ids of tile t.  Every load here and in fetch_data is
@@ -105,12 +114,12 @@ struct KvTile {
       const uint8_t* vb = v_head + slot0 * v_slot_bytes;
 #pragma unroll
       for (int k = 0; k < KU; ++k) {
-        const uint8_t* src = readable(tc * kTileKeys + k_row(k)) ? kb + k_off[k] : g_zero_row;
+        const uint8_t* src = k_has(k) && readable(tc * kTileKeys + k_row(k)) ? kb + k_off[k] : g_zero_row;
         st.k[k] = *reinterpret_cast<const u32x4*>(src);
       }
 #pragma unroll
       for (int k = 0; k < VU; ++k) {
-        const uint8_t* src = readable(tc * kTileKeys + v_key(k)) ? vb + v_off[k] : g_zero_row;
+        const uint8_t* src = v_has(k) && readable(tc * kTileKeys + v_key(k)) ? vb + v_off[k] : g_zero_row;
         st.v[k] = *reinterpret_cast<const u32x4*>(src);
       }
       return;
@@ -119,14 +128,14 @@ struct KvTile {
     for (int k = 0; k < KU; ++k) {
       const int j = tc * kTileKeys + k_row(k);
       const size_t slot = ((size_t)(UPAGE ? p.k[0] : p.k[k]) << lp) | (size_t)(j & pmask);
-      const uint8_t* src = readable(j) ? k_head + slot * k_slot_bytes + k_piece(k) * 16 : g_zero_row;
+      const uint8_t* src = k_has(k) && readable(j) ? k_head + slot * k_slot_bytes + k_piece(k) * 16 : g_zero_row;
       st.k[k] = *reinterpret_cast<const u32x4*>(src);
     }
 #pragma unroll
     for (int k = 0; k < VU; ++k) {
       const int j = tc * kTileKeys + v_key(k);
       const size_t slot = ((size_t)(UPAGE ? p.v[0] : p.v[k]) << lp) | (size_t)(j & pmask);
-      const uint8_t* src = readable(j) ? v_head + slot * v_slot_bytes + v_piece(k) * 16 : g_zero_row;
+      const uint8_t* src = v_has(k) && readable(j) ? v_head + slot * v_slot_bytes + v_piece(k) * 16 : g_zero_row;
       st.v[k] = *reinterpret_cast<const u32x4*>(src);
     }
   }
@@ -135,6 +144,7 @@ struct KvTile {
   __device__ __forceinline__ void store(const Stage& st, uint16_t* k_lds, uint16_t* v_lds) const {
 #pragma unroll
     for (int k = 0; k < KU; ++k) {
+      if (!k_has(k)) continue;
       const int row = k_row(k), piece = k_piece(k);
       if constexpr (FP8) {
         const u32x2 c0 = e4m3x4_to_bf16x4(st.k[k].x), c1 = e4m3x4_to_bf16x4(st.k[k].y);
@@ -148,6 +158,7 @@ struct KvTile {
     }
 #pragma unroll
     for (int k = 0; k < VU; ++k) {
+      if (!v_has(k)) continue;
       const int key = v_key(k), piece = v_piece(k);
       if constexpr (FP8) {
         const u32x2 c0 = e4m3x4_to_bf16x4(st.v[k].x), c1 = e4m3x4_to_bf16x4(st.v[k].y);
