@@ -14,9 +14,11 @@ The KV pool is replicated into enough copies ("layers") to exceed 1 GiB, and
 consecutive steps read consecutive copies, so no step finds its keys in the
 256 MB Infinity Cache or the L2.  Inputs are resident in HBM before timing.
 
-One JSON line is printed.  `roofline` is the main attention kernel alone:
-its duration comes from HIP events the library records around that kernel
-(diffkv_attn_profile_next_call), averaged over the timed steps.
+One JSON line is printed.  `value` and `ms_per_step` come from the timed
+steps alone (HIP events around the K calls, no per-call instrumentation).
+`roofline` is the main attention kernel alone: a second pass of the same K
+calls has the library's dispatch stamp each main kernel with HIP events
+(diffkv_attn_profile_next_call); their mean is the kernel's duration.
 `cpu_baseline` times the FP64 oracle on the host on a bounded sample.
 `extra` carries the other workloads measured the same way.
 """
@@ -155,15 +157,21 @@ def measure(name, steps, warmup, events, target_bytes=1 << 30):
     for i in range(warmup):
         calls[i % layers]()
     torch.cuda.synchronize()
+    # Timed region: exactly `steps` calls, nothing else on the stream.
     wall0 = time.perf_counter()
     events.record(t0, stream)
     for k in range(steps):
-        B.diffkv_attn_profile_next_call(pairs[k][0], pairs[k][1])
         calls[k % layers]()
     events.record(t1, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = events.elapsed_ms(t0, t1)
+    # Second pass, same calls: the library stamps each main kernel's dispatch
+    # with a pair of events, giving that kernel's own duration.
+    for k in range(steps):
+        B.diffkv_attn_profile_next_call(pairs[k][0], pairs[k][1])
+        calls[k % layers]()
+    torch.cuda.synchronize()
     kern = sorted(events.elapsed_ms(a, b) for a, b in pairs)
     out = calls[(steps - 1) % layers].out
     if not bool(torch.isfinite(out.float()).all()):

@@ -225,7 +225,8 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
       fp8 ? dispatch_split<true>(a, plan.row_tiles, upage, grid, direct, count_out != nullptr, stream)
           : dispatch_split<false>(a, plan.row_tiles, upage, grid, direct, count_out != nullptr, stream);
   if (e == hipSuccess && !direct)
-    e = launch_merge(a, plan.rows, dim3(plan.n_qtiles * plan.rows, d->batch * d->num_kv_heads), stream);
+    e = launch_merge(a, plan.rows,
+                     dim3(d->max_q_len * G, d->batch * d->num_kv_heads), stream);
   return e == hipSuccess ? DIFFKV_OK : DIFFKV_HIP_ERROR;
 }
 

@@ -84,7 +84,13 @@ void split_attn_kernel(const SplitArgs a) {
   int kv_lo, kv_hi, t_begin, t_end, n_valid;
   qtile_key_range(L, n, G, qt, ROWS, a.window, kv_lo, kv_hi);
   split_tiles(kv_lo, kv_hi, a.num_splits, s, t_begin, t_end, n_valid);
-  if (t_begin >= t_end) return;
+  if (t_begin >= t_end) {
+    // An empty split still marks its rows (log-sum-exp -inf) so the merge can
+    // read every split without knowing which ones had keys.
+    if (!DIRECT && tid < ROWS && qt * ROWS + tid < n * G)
+      a.part_lse[(((size_t)bg * a.n_qtiles + qt) * a.num_splits + s) * ROWS + tid] = -INFINITY;
+    return;
+  }
 
   const IO io(a.k_cache, a.v_cache, a.block_table + (size_t)b * a.bt_stride, a.hkv, g,
               a.log2_page, kv_lo, kv_hi, t_end, tid);
@@ -294,69 +300,67 @@ __device__ __forceinline__ float wave_sum_all(float v) {
 
 // Combines the split partials of one query row: weights 2^(lse_s - M), the
 // sink joining the denominator, v_scale, bf16 store.  One 256-thread
-// workgroup per row.  Lanes read 64 splits' lse values at a time; wave w
-// then takes splits w, w+4, ... of that group with all sixteen of its
-// partial-row loads (two output dims per lane) in flight together, and the
-// four partial sums meet in LDS in a fixed order (deterministic).
+// workgroup per row.  Every split wrote its row (an empty split an lse of
+// -inf), so the lse values and the partial rows are all loaded at once, with
+// no dependence on the sequence lengths: per group of 64 splits each lane
+// reads one lse and wave w the partial rows of splits w, w+4, ... (two output
+// dims per lane).  Groups are combined with a running maximum; the four
+// waves' sums meet in LDS in a fixed order (deterministic).
 template <int ROWS>
 __global__ __launch_bounds__(256) void split_merge_kernel(const SplitArgs a) {
   __shared__ f32x2 red[3][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int qt = blockIdx.x / ROWS, r = blockIdx.x % ROWS;
+  const int R = blockIdx.x;                 // row of this (sequence, KV head)
+  const int qt = R / ROWS, r = R % ROWS;
   const int bg = blockIdx.y;
   const int b = bg / a.hkv, g = bg % a.hkv;
   const int G = a.group;
-  const int L = a.seq_lens[b];
+  const int S = a.num_splits;
   const int n = a.q_lens ? a.q_lens[b] : 1;
-  const int R = qt * ROWS + r;
-  if (R >= n * G) return;
-  int kv_lo, kv_hi, t_begin, t_end, n_valid;
-  qtile_key_range(L, n, G, qt, ROWS, a.window, kv_lo, kv_hi);
-  split_tiles(kv_lo, kv_hi, a.num_splits, 0, t_begin, t_end, n_valid);
-  const int tok = R / G, h = g * G + R % G;
-  const float s2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
+  const int r0 = seq_row_start(a.q_lens, b);
 
-  const size_t prow0 = ((size_t)bg * a.n_qtiles + qt) * a.num_splits * ROWS + r;
-  // Pass over groups of 64 splits; the common case (<= 64 splits) is one pass.
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < n_valid; s0 += 64)
-    if (s0 + lane < n_valid) M = fmaxf(M, a.part_lse[prow0 + (size_t)(s0 + lane) * ROWS]);
-  M = wave_max_all(M);
-  const float Mt = fmaxf(M, s2);
-
+  const size_t prow0 = ((size_t)bg * a.n_qtiles + qt) * S * ROWS + r;
+  float m_run = -INFINITY, ksum = 0.f;
   f32x2 acc = f32x2{0.f, 0.f};
-  float ksum = 0.f;
-  for (int s0 = 0; s0 < n_valid; s0 += 64) {
-    const int sl = s0 + lane;
-    const float wl = sl < n_valid ? fast_exp2(a.part_lse[prow0 + (size_t)sl * ROWS] - Mt) : 0.f;
-    ksum += wl;
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int cnt = min(64, S - s0);
+    const float lse_l = lane < cnt ? a.part_lse[prow0 + (size_t)(s0 + lane) * ROWS] : -INFINITY;
     const float* po = a.part_o + (prow0 + (size_t)s0 * ROWS) * kHeadDimV + 2 * lane;
     f32x2 v[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int i = min(wave + 4 * k, 63);
-      v[k] = *reinterpret_cast<const f32x2*>(po + (size_t)min(i, n_valid - 1 - s0) * ROWS * kHeadDimV);
-    }
+    for (int k = 0; k < 16; ++k)
+      v[k] = *reinterpret_cast<const f32x2*>(po + (size_t)min(wave + 4 * k, cnt - 1) * ROWS * kHeadDimV);
+    const float m_new = fmaxf(m_run, wave_max_all(lse_l));
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float f = fast_exp2(m_run - m_use);
+    acc *= f;
+    ksum *= f;
+    const float wl = fast_exp2(lse_l - m_use);
+    ksum += wl;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int i = wave + 4 * k;
       const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), min(i, 63)));
-      if (s0 + i < n_valid) acc += w * v[k];
+      if (i < cnt && w > 0.f) acc += w * v[k];
     }
+    m_run = m_new;
   }
   if (wave > 0) red[wave - 1][lane] = acc;
   __syncthreads();
-  if (wave > 0) return;
+  if (wave > 0 || R >= n * G) return;
   acc += red[0][lane];
   acc += red[1][lane];
   acc += red[2][lane];
   ksum = wave_sum_all(ksum);
-  const int r0 = seq_row_start(a.q_lens, b);
-  const float den = ksum + (a.sinks ? fast_exp2(s2 - Mt) : 0.f);
-  const float coef = a.v_scale / den;
+  const int tok = R / G, h = g * G + R % G;
+  const float s2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
+  const float Mt = fmaxf(m_run, s2);
+  const float f = fast_exp2(m_run - Mt);
+  const float den = ksum * f + (a.sinks ? fast_exp2(s2 - Mt) : 0.f);
+  const float coef = a.v_scale * f / den;
   const size_t out_row = (size_t)(r0 + tok) * a.hq + h;
   *reinterpret_cast<uint32_t*>(a.out + out_row * kHeadDimV + 2 * lane) = pack_bf16x2(acc.x * coef, acc.y * coef);
-  if (a.lse_out && lane == 0) a.lse_out[out_row] = (Mt + log2f(ksum)) * kLn2;
+  if (a.lse_out && lane == 0) a.lse_out[out_row] = (m_run + log2f(ksum)) * kLn2;
 }
 
 __global__ void fill_i32_kernel(int32_t* p, size_t n, int32_t v) {

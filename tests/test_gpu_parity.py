@@ -151,3 +151,28 @@ def test_fp8_values_pass_through_exactly(entry):
     want = decode_e4m3fn(rows)
     for h in range(2):
         assert np.array_equal(got[:, h, :], want), "E4M3 decode is not exact on the GPU"
+
+
+@pytest.mark.parametrize("q_len,hq,splits", [(1, 8, 0), (1, 8, 9), (4, 8, 5), (8, 8, 40)])
+def test_workspace_reuse_across_calls(q_len, hq, splits):
+    """One workspace, several calls with different sequence lengths inside the
+    same descriptor bounds: the split partials and the arrival counters the
+    last split uses to merge must leave the workspace ready for the next call
+    (both the fused-merge and the merge-kernel paths)."""
+    from paged_asymmetric_head_amd import binding as B
+    entry = "decode" if q_len == 1 else "verify"
+    lens = [[3000, 2500, 700], [2999, 64, 3001], [1, 3001, 1500]]
+    base = make_paged_inputs(61, seq_lens=lens[0], q_lens=q_len, num_q_heads=hq, num_kv_heads=1,
+                             page_size=128, kv_dtype="bf16", max_seq_len=3001)
+    dev0 = DeviceInputs(base)
+    ws, nbytes = dev0.workspace_for(entry, splits)
+    say(f"workspace reuse: {entry} q_len={q_len} splits={splits} ws={nbytes} "
+        f"num_splits={B.diffkv_attn_num_splits(dev0.desc(entry, splits), B.ENTRIES[entry])}")
+    for k, L in enumerate(lens):
+        Lq = [max(x, q_len) for x in L]
+        inp = make_paged_inputs(61 + k, seq_lens=Lq, q_lens=q_len, num_q_heads=hq, num_kv_heads=1,
+                                page_size=128, kv_dtype="bf16", max_seq_len=3001)
+        dev = DeviceInputs(inp)
+        out, _, _ = dev.run(entry, force_num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        compare(to_np(out), oracle(inp).out, f"reuse call {k}")
