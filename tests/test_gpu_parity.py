@@ -176,3 +176,120 @@ def test_workspace_reuse_across_calls(q_len, hq, splits):
         out, _, _ = dev.run(entry, force_num_splits=splits, workspace=ws)
         torch.cuda.synchronize()
         compare(to_np(out), oracle(inp).out, f"reuse call {k}")
+
+
+# --- adversarial: which slots are read ------------------------------------------
+
+def _poison_pages_before_window(inp):
+    """Block-table entries of pages wholly before every token's window -> -1."""
+    bt = inp.block_table.copy()
+    for b in range(inp.batch):
+        L, n = int(inp.seq_lens[b]), int(inp.q_lens[b])
+        first_key = max(0, L - n - inp.window + 1)
+        bt[b, :first_key // inp.page_size] = -1
+    inp.block_table = bt
+    return inp
+
+
+@pytest.mark.parametrize("P,kv", [(1, "fp8"), (16, "bf16"), (128, "fp8")])
+def test_unmapped_pages_before_the_window_are_never_read(P, kv):
+    inp = make_paged_inputs(95, seq_lens=[700, 131, 4000], q_lens=[4, 4, 4], num_q_heads=8,
+                            num_kv_heads=1, page_size=P, kv_dtype=kv, window=128, sinks=True,
+                            write_align=128)
+    _poison_pages_before_window(inp)
+    dev = DeviceInputs(inp)
+    for entry in ("verify", "prefill"):
+        check_call(dev, entry, f"unmapped-before-window P={P} {kv}")
+
+
+def _plant(inp, b, j, row_tokens, scale=60.0):
+    """Make key j of sequence b score far above every other key for the query
+    rows of `row_tokens` (packed rows), every head of KV head 0, and give it a
+    distinctive value row.  Works on the bf16 cache in place."""
+    from oracle import decode_bf16
+    from paged_asymmetric_head_amd.synth import to_bf16_bits
+    page, slot = inp.block_table[b, j // inp.page_size], j % inp.page_size
+    q = decode_bf16(inp.q[row_tokens, :, :]).mean(axis=(0, 1))
+    k = scale * q / np.linalg.norm(q) * np.sqrt(192)
+    inp.k_cache[page, slot, 0, :] = to_bf16_bits(k.astype(np.float32))
+    inp.v_cache[page, slot, 0, :] = to_bf16_bits(np.full(128, 7.0, dtype=np.float32))
+
+
+@pytest.mark.parametrize("where", ["future_in_block", "before_window", "past_end"])
+def test_planted_dominant_keys_outside_the_mask_are_ignored(where):
+    """A key just outside a row's visible range that would dominate the softmax
+    if it were read: the output must still match the oracle (which excludes
+    it), so an off-by-one in any boundary fails loudly."""
+    W = 40 if where == "before_window" else 0
+    inp = make_paged_inputs(97, seq_lens=[200, 96], q_lens=[8, 8], num_q_heads=4, num_kv_heads=1,
+                            page_size=16, kv_dtype="bf16", window=W, write_align=16 if W else None,
+                            extra_pages=2)
+    b, L, n = 0, 200, 8
+    if where == "future_in_block":
+        j, rows = L - n + 3, [0, 1, 2]            # key of token 3, seen by none of tokens 0..2
+    elif where == "before_window":
+        j, rows = L - n - W, [0]                   # one before token 0's window start
+    else:
+        # the slot one past the sequence end: 200 % 16 == 8, so it lies in the
+        # sequence's last page (slot 8) and holds no token
+        j, rows = L, list(range(n))
+    _plant(inp, b, j, rows)
+    dev = DeviceInputs(inp)
+    for entry in ("verify", "prefill"):
+        check_call(dev, entry, f"planted {where}")
+
+
+def test_planted_dominant_key_just_inside_dominates():
+    inp = make_paged_inputs(98, seq_lens=[200], q_lens=8, num_q_heads=4, num_kv_heads=1,
+                            page_size=16, kv_dtype="bf16", window=40, write_align=16)
+    L, n, W = 200, 8, 40
+    j = L - n - W + 1                               # token 0's first visible key
+    _plant(inp, 0, j, [0])
+    dev = DeviceInputs(inp)
+    out = check_call(dev, "verify", "planted inside")
+    assert float(out[0, 0, 0].float()) > 6.0        # token 0 is dominated by the planted value 7
+
+
+# --- graph capture and replay ----------------------------------------------------
+
+def test_hip_graph_replay_with_new_lengths_and_tables():
+    """Capture one verify call (split-KV + merge) in a HIP graph and replay it
+    after changing seq_lens, q_lens and block_table in place (within the
+    descriptor's bounds), with eager work and synchronisation between
+    replays; every replay must match the oracle for the new contents."""
+    base = make_paged_inputs(101, seq_lens=[900, 1500, 64], q_lens=[4, 4, 4], num_q_heads=8,
+                             num_kv_heads=1, page_size=16, kv_dtype="bf16", window=0, sinks=True,
+                             max_seq_len=1600, extra_pages=400)
+    dev = DeviceInputs(base)
+    d = dev.desc("verify")
+    ws, nbytes = dev.workspace_for("verify")
+    out = torch.empty((base.total_q, 8, 128), dtype=torch.bfloat16, device="cuda")
+    from paged_asymmetric_head_amd import binding as B
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.diffkv_attn_verify(d, dev.q, dev.k_cache, dev.v_cache, dev.block_table, dev.seq_lens,
+                             dev.q_lens, base.window, dev.sinks, base.k_scale, base.v_scale,
+                             base.softmax_scale, out, None, None, ws, nbytes)
+    rng = np.random.default_rng(5)
+    for rep in range(4):
+        # New lengths within bounds, reusing the same pool: rebuild a workload whose
+        # pages fit the pool, then copy its tables and data into the captured buffers.
+        lens = [int(x) for x in rng.integers(4, 1600, size=3)]
+        inp = make_paged_inputs(200 + rep, seq_lens=lens, q_lens=[4, 4, 4], num_q_heads=8,
+                                num_kv_heads=1, page_size=16, kv_dtype="bf16", sinks=True,
+                                max_seq_len=1600,
+                                extra_pages=base.num_pages - sum(-(-x // 16) for x in lens))
+        assert inp.num_pages == base.num_pages
+        inp.sinks = base.sinks
+        dev.q.copy_(torch.from_numpy(inp.q.view(np.int16)))
+        dev.k_cache.copy_(torch.from_numpy(inp.k_cache.view(np.int16)))
+        dev.v_cache.copy_(torch.from_numpy(inp.v_cache.view(np.int16)))
+        dev.block_table.copy_(torch.from_numpy(inp.block_table))
+        dev.seq_lens.copy_(torch.from_numpy(inp.seq_lens))
+        torch.cuda.synchronize()
+        say(f"graph replay {rep}: seq_lens={lens}")
+        g.replay()
+        torch.cuda.synchronize()
+        compare(to_np(out), oracle(inp).out, f"graph replay {rep}")
+        _ = (dev.q.float() * 2).sum().item()     # eager work between replays
