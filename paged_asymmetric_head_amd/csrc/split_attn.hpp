@@ -134,6 +134,16 @@ void split_attn_kernel(const SplitArgs a) {
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   int cnt = 0;
 
+  // Tiles every row of the workgroup sees whole (no key past the first row's
+  // position, none before the last row's window start) skip the mask.
+  // Padding rows past n*G may then score keys they would not see; their
+  // results stay in their own lanes and are never written.
+  const int r_first = qt * ROWS;
+  const int r_last = min(n * G, r_first + ROWS) - 1;
+  const int p_first = L - n + r_first / G;
+  const int lo_last = a.window > 0 ? max(0, L - n + r_last / G - a.window + 1) : 0;
+  const float scale = a.scale_log2;   // > 0 (checked on the host)
+
   // One online-softmax update per tile: the S^T tiles of all this wave's
   // 16-key subtiles first (independent MFMA chains), one max / rescale / sum
   // over them, then all the P*V products.
@@ -149,54 +159,60 @@ void split_attn_kernel(const SplitArgs a) {
         sacc[sub] = mfma_16x16x32(*reinterpret_cast<const u32x4*>(kp), qreg[c], sacc[sub]);
       }
 
-    // sacc[sub][i] = S^T[key (kg*SUBS+sub)*16 + 4*grp + i][row col].  Masked by select only.
-    float x[SUBS][4];
+    // sacc[sub][i] = raw S^T[key (kg*SUBS+sub)*16 + 4*grp + i][row col].
+    // The branch is uniform over the workgroup.
+    if (t * kTileKeys < lo_last || t * kTileKeys + kTileKeys - 1 > p_first) {
+#pragma unroll
+      for (int sub = 0; sub < SUBS; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = t * kTileKeys + (kg * SUBS + sub) * 16 + 4 * grp + i;
+          const bool vis = j >= lo_row && j <= hi_row;
+          sacc[sub][i] = vis ? sacc[sub][i] : -INFINITY;
+          if constexpr (COUNT) cnt += vis ? 1 : 0;
+        }
+    } else {
+      if constexpr (COUNT) cnt += 4 * SUBS;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < SUBS; ++sub)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = t * kTileKeys + (kg * SUBS + sub) * 16 + 4 * grp + i;
-        const bool vis = j >= lo_row && j <= hi_row;
-        x[sub][i] = vis ? sacc[sub][i] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, x[sub][i]);
-        if constexpr (COUNT) cnt += vis ? 1 : 0;
-      }
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[sub][i]);
     mx = wave_max_xor(mx, 16);
     mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m, mx);
+    const float m_new = fmaxf(m, mx * scale);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
-    float ps = 0.f;
     u32x2 pb[SUBS];
 #pragma unroll
     for (int sub = 0; sub < SUBS; ++sub) {
       float pr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pr[i] = fast_exp2(x[sub][i] - m_use);
-        ps += pr[i];
-      }
+      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(__builtin_fmaf(sacc[sub][i], scale, -m_use));
       pb[sub] = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
     }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l = l * alpha + ps;
     m = m_new;
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
-    for (int nn = 0; nn < 8; ++nn) o[nn] *= alpha;
+      for (int nn = 0; nn < 8; ++nn) o[nn] *= alpha;
+    }
 
     // V^T operand straight from the row-major tile: in each 16-lane group the
     // transposing read hands lane col the dim 16*nn + col of keys
     // 4*grp + 0..3 when source lane col reads 4 dims (16*nn + 4*(col%4))
-    // of key 4*grp + col/4.
+    // of key 4*grp + col/4.  The row sums of the (bf16) P come from an extra
+    // all-ones V^T tile: every element of psum is sum_k P[row][k].
+    f32x4 psum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sub = 0; sub < SUBS; ++sub) {
       const uint16_t* vp = v_lds + ((kg * SUBS + sub) * 16 + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
 #pragma unroll
       for (int nn = 0; nn < 8; ++nn)
         o[nn] = mfma_16x16x16(lds_read_tr16(vp + 16 * nn), pb[sub], o[nn]);
+      psum = mfma_16x16x16(kOnesBf16x4, pb[sub], psum);
     }
+    l = __builtin_fmaf(l, alpha, psum[0]);
   };
 
   // Every stage step runs in every round (loads stay in one fixed order, so
