@@ -22,7 +22,9 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // S/O tiles: D(16x16, fp32) += A(16 x K) * B(K x 16) on the matrix cores.
 // Operand layout shared by both shapes: lane l supplies row (l % 16) of A and
 // column (l % 16) of B, its lane group (l / 16) a slice of the contraction;
-// D comes back as rows 4*(l/16)+i, column l%16 for i = 0..3.
+// D comes back as rows 4*(l/16)+i, column l%16 for i = 0..3.  On gfx950 one
+// 16x16x16 takes about as long as one 16x16x32 (half the rate), so the
+// contractions use K = 32 wherever a wave holds 32 keys.
 __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -32,8 +34,11 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
-// Four bf16 ones, an MFMA operand that sums the other operand's columns.
+// Four / eight bf16 ones: MFMA operands that sum the other operand's columns.
 constexpr u32x2 kOnesBf16x4 = u32x2{0x3F803F80u, 0x3F803F80u};
+constexpr u32x4 kOnesBf16x8 = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+
+__device__ __forceinline__ u32x4 cat(u32x2 lo, u32x2 hi) { return u32x4{lo.x, lo.y, hi.x, hi.y}; }
 
 // gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of
 // 16 lanes the four 16-bit values each lane reads are concatenated in lane

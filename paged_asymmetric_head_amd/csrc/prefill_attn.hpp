@@ -11,7 +11,7 @@
 // tile t from the other.  Per tile each wave runs
 //   S^T = K * Q^T   (16x16x32 bf16 MFMA, 4 key subtiles x 6)
 //   one online-softmax update (rows live in lanes; keys across lane groups)
-//   O^T += V^T P^T  (16x16x16 bf16 MFMA, 4 x 8), V^T from the transposing
+//   O^T += V^T P^T  (16x16x32 bf16 MFMA, 2 x 8), V^T from the transposing
 //                    LDS read of the row-major V tile.
 // Only tiles that cross a row's causal or window boundary (or hold padding
 // rows) are masked; the others skip the compares.  The exp argument folds
@@ -171,16 +171,22 @@ void prefill_attn_kernel(const SplitArgs a) {
       for (int nn = 0; nn < 8; ++nn) o[nn] *= alpha;
     }
 
-    // The row sums of this tile's (bf16) P come from the matrix cores too: an
-    // all-ones V^T tile gives sum_k P[row][k] in every element, across all
-    // four lane groups, with no shuffles.
+    // O^T += V^T P^T over 32 keys per step: lane group grp contracts keys
+    // 32c + 4grp + 0..3 and 32c + 16 + 4grp + 0..3, the P values it already
+    // holds for subtiles 2c and 2c+1, and the matching V^T values come from
+    // two transposing reads.  The row sums of this tile's (bf16) P come from
+    // the matrix cores too: an all-ones V^T tile gives sum_k P[row][k] in
+    // every element, across all four lane groups, with no shuffles.
     f32x4 psum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      const uint16_t* vp = v_lds + (sub * 16 + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
+    for (int c = 0; c < 2; ++c) {
+      const u32x4 pt = cat(pb[2 * c], pb[2 * c + 1]);
+      const uint16_t* vp = v_lds + (32 * c + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn) o[nn] = mfma_16x16x16(lds_read_tr16(vp + 16 * nn), pb[sub], o[nn]);
-      psum = mfma_16x16x16(kOnesBf16x4, pb[sub], psum);
+      for (int nn = 0; nn < 8; ++nn)
+        o[nn] = mfma_16x16x32(cat(lds_read_tr16(vp + 16 * nn), lds_read_tr16(vp + 16 * kVLdsStride + 16 * nn)),
+                              pt, o[nn]);
+      psum = mfma_16x16x32(kOnesBf16x8, pt, psum);
     }
     l = __builtin_fmaf(l, alpha, psum[0]);
   };

@@ -17,7 +17,9 @@
 //   S^T = K * Q^T        (v_mfma_f32_16x16x32_bf16, 6 steps over 192 dims)
 //   mask -> online softmax in base 2 (rows live in lanes, keys across the
 //           4 lane groups: two xor-shuffles per reduction)
-//   O^T += V^T * P^T     (v_mfma_f32_16x16x16_bf16, 8 tiles over 128 dims)
+//   O^T += V^T * P^T     (v_mfma_f32_16x16x32_bf16 when a wave holds 32 or
+//                         more keys of the tile, else 16x16x16; 8 tiles over
+//                         the 128 dims)
 // Keeping S and O transposed puts one query row in each lane, so the softmax
 // rescale needs no data movement between lanes.
 // The global loads of the next NS tiles are in flight in registers while a
@@ -203,14 +205,31 @@ void split_attn_kernel(const SplitArgs a) {
     // 4*grp + 0..3 when source lane col reads 4 dims (16*nn + 4*(col%4))
     // of key 4*grp + col/4.  The row sums of the (bf16) P come from an extra
     // all-ones V^T tile: every element of psum is sum_k P[row][k].
+    // With two or more subtiles per wave the products contract 32 keys at a
+    // time: lane group grp takes keys 4grp + 0..3 of subtiles 2c and 2c+1 (the
+    // P values it holds), and two transposing reads give the matching V^T.
     f32x4 psum = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (SUBS % 2 == 0) {
 #pragma unroll
-    for (int sub = 0; sub < SUBS; ++sub) {
-      const uint16_t* vp = v_lds + ((kg * SUBS + sub) * 16 + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
+      for (int c = 0; c < SUBS / 2; ++c) {
+        const u32x4 pt = cat(pb[2 * c], pb[2 * c + 1]);
+        const uint16_t* vp =
+            v_lds + ((kg * SUBS + 2 * c) * 16 + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn)
-        o[nn] = mfma_16x16x16(lds_read_tr16(vp + 16 * nn), pb[sub], o[nn]);
-      psum = mfma_16x16x16(kOnesBf16x4, pb[sub], psum);
+        for (int nn = 0; nn < 8; ++nn)
+          o[nn] = mfma_16x16x32(cat(lds_read_tr16(vp + 16 * nn), lds_read_tr16(vp + 16 * kVLdsStride + 16 * nn)),
+                                pt, o[nn]);
+        psum = mfma_16x16x32(kOnesBf16x8, pt, psum);
+      }
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < SUBS; ++sub) {
+        const uint16_t* vp = v_lds + ((kg * SUBS + sub) * 16 + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn)
+          o[nn] = mfma_16x16x16(lds_read_tr16(vp + 16 * nn), pb[sub], o[nn]);
+        psum = mfma_16x16x16(kOnesBf16x4, pb[sub], psum);
+      }
     }
     l = __builtin_fmaf(l, alpha, psum[0]);
   };
