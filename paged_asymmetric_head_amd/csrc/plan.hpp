@@ -110,7 +110,7 @@ inline SplitPlan plan_split(const diffkv_attn_desc& d, int window, bool allow_sp
 
 // Prefill: workgroups of kPrefillRows query rows along one (sequence, KV
 // head), one 16-row tile per wave.
-constexpr int kPrefillRows = 128;
+constexpr int kPrefillRows = 256;
 inline int prefill_row_blocks(const diffkv_attn_desc& d) {
   return ceil_div((long long)d.max_q_len * (d.num_q_heads / d.num_kv_heads), kPrefillRows);
 }

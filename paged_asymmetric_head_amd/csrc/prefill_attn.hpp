@@ -3,16 +3,20 @@
 // "diffbot/MiMo-V2.6-Flash-RL-FP8KV-W4A8-2x-RTX-PRO-6000", What the kernels
 // do: the prefill rows of a 4096-token chunk at 26K context, one block of
 // 8 tokens x 16 GQA heads per program, FP8 K/V converted on the way in.
-// Here a 512-thread workgroup owns 128 query rows of one (sequence, KV head)
+// Here a 512-thread workgroup owns 256 query rows of one (sequence, KV head)
 // -- row r is new token r / G and query head g*G + r % G, so at G = 16 that
-// is 8 tokens x 16 heads -- one 16-row tile per wave, two waves per SIMD, one
-// workgroup per CU.  The 64-key K/V tiles are double-buffered in LDS: tile
-// t + 1 is gathered and widened into one buffer while the matrix cores read
-// tile t from the other.  Per tile each wave runs
+// is 16 tokens x 16 heads -- two 16-row tiles per wave, two waves per SIMD,
+// one workgroup per CU.  The 64-key K/V tiles are double-buffered in LDS:
+// tile t + 1 is gathered and widened into one buffer while the matrix cores
+// read tile t from the other.  Per tile each wave runs, for both its row
+// tiles,
 //   S^T = K * Q^T   (16x16x32 bf16 MFMA, 4 key subtiles x 6)
 //   one online-softmax update (rows live in lanes; keys across lane groups)
 //   O^T += V^T P^T  (16x16x32 bf16 MFMA, 2 x 8), V^T from the transposing
 //                    LDS read of the row-major V tile.
+// Each K or V^T fragment read from LDS feeds the MFMAs of both row tiles:
+// on gfx950 LDS read bandwidth, not the matrix cores, bounds a wave that
+// reads the whole tile for only 16 rows.
 // Only tiles that cross a row's causal or window boundary (or hold padding
 // rows) are masked; the others skip the compares.  The exp argument folds
 // the scale into one FMA on the raw score (the scale is positive), the row
@@ -22,15 +26,13 @@
 // merge; row blocks are issued latest-token first (they are the longest).
 #pragma once
 
-#include <type_traits>
-
 #include "kv_tile.hpp"
 #include "split_attn.hpp"
 
 namespace diffkv {
 
-constexpr int kPfRows = kPrefillRows;   // query rows per prefill workgroup
-constexpr int kPfWaves = kPfRows / 16;   // one 16-row tile per wave
+constexpr int kPfRowTiles = 2;                               // 16-row tiles per wave
+constexpr int kPfWaves = kPrefillRows / (16 * kPfRowTiles);  // waves per workgroup
 constexpr int kPfThreads = 64 * kPfWaves;
 #ifndef DIFFKV_PREFILL_STAGES
 #define DIFFKV_PREFILL_STAGES 2
@@ -41,6 +43,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 8
 void prefill_attn_kernel(const SplitArgs a) {
   using IO = KvTile<FP8, UPAGE, kPfThreads>;
   constexpr int NS = DIFFKV_PREFILL_STAGES;
+  constexpr int RT = kPfRowTiles;
   constexpr int LDS_TILE = kKLdsElems + kVLdsElems;
 
   // Two LDS tiles: the next tile is widened into one while the matrix cores
@@ -57,17 +60,17 @@ void prefill_attn_kernel(const SplitArgs a) {
 
   const int L = a.seq_lens[b];
   const int n = a.q_lens ? a.q_lens[b] : 1;
-  if (qb * kPfRows >= n * G) return;
+  if (qb * kPrefillRows >= n * G) return;
   int kv_lo, kv_hi;
-  qtile_key_range(L, n, G, qb, kPfRows, a.window, kv_lo, kv_hi);
+  qtile_key_range(L, n, G, qb, kPrefillRows, a.window, kv_lo, kv_hi);
   const int t_begin = kv_lo / kTileKeys;
   const int t_end = (kv_hi + kTileKeys - 1) / kTileKeys;
 
   // Tiles every row of the block sees whole: no key past the first row's
   // position, none before the last row's window start, no padding rows.
-  const int r_first = qb * kPfRows;
-  const int r_last = min(n * G, r_first + kPfRows) - 1;
-  const bool has_pad = r_first + kPfRows > n * G;
+  const int r_first = qb * kPrefillRows;
+  const int r_last = min(n * G, r_first + kPrefillRows) - 1;
+  const bool has_pad = r_first + kPrefillRows > n * G;
   const int p_first = L - n + r_first / G;
   const int p_last = L - n + r_last / G;
   const int lo_last = a.window > 0 ? max(0, p_last - a.window + 1) : 0;
@@ -87,21 +90,24 @@ void prefill_attn_kernel(const SplitArgs a) {
 
   const int r0 = seq_row_start(a.q_lens, b);
 
-  // This lane's query row.
-  const int R = r_first + wave * 16 + col;
-  const bool row_ok = R < n * G;
-  const int tok = row_ok ? R / G : 0;
-  const int hh = g * G + (row_ok ? R % G : 0);
-  const int p_row = L - n + tok;
-  const int lo_row = a.window > 0 ? max(0, p_row - a.window + 1) : 0;
-  const int hi_row = row_ok ? p_row : -1;
-  u32x4 qreg[6];
-  {
-    const uint16_t* qp = a.q + ((size_t)(r0 + tok) * a.hq + hh) * kHeadDimQK + 8 * grp;
+  // This lane's query row in each of the wave's row tiles.
+  bool row_ok[RT];
+  int tok[RT], hh[RT], lo_row[RT], hi_row[RT];
+  u32x4 qreg[RT][6];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int R = r_first + (wave * RT + rt) * 16 + col;
+    row_ok[rt] = R < n * G;
+    tok[rt] = row_ok[rt] ? R / G : 0;
+    hh[rt] = g * G + (row_ok[rt] ? R % G : 0);
+    const int p_row = L - n + tok[rt];
+    lo_row[rt] = a.window > 0 ? max(0, p_row - a.window + 1) : 0;
+    hi_row[rt] = row_ok[rt] ? p_row : -1;
+    const uint16_t* qp = a.q + ((size_t)(r0 + tok[rt]) * a.hq + hh[rt]) * kHeadDimQK + 8 * grp;
 #pragma unroll
     for (int c = 0; c < 6; ++c)
-      qreg[c] = *reinterpret_cast<const u32x4*>(row_ok ? reinterpret_cast<const uint8_t*>(qp + 32 * c)
-                                                       : g_zero_row);
+      qreg[rt][c] = *reinterpret_cast<const u32x4*>(
+          row_ok[rt] ? reinterpret_cast<const uint8_t*>(qp + 32 * c) : g_zero_row);
   }
 
   // Tile t lives in LDS buffer t & 1 and, before that, in register stage
@@ -114,61 +120,84 @@ void prefill_attn_kernel(const SplitArgs a) {
   io.fetch_pages(t_begin + 2 * NS, pg[0]);
   __syncthreads();
 
-  float m = -INFINITY, l = 0.f;
-  f32x4 o[8];
+  float m[RT], l[RT];
+  f32x4 o[RT][8];
+  int cnt[RT];
 #pragma unroll
-  for (int nn = 0; nn < 8; ++nn) o[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int cnt = 0;
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = -INFINITY;
+    l[rt] = 0.f;
+    cnt[rt] = 0;
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) o[rt][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const float scale = a.scale_log2;   // > 0 (checked on the host)
 
-  auto compute_tile = [&](int t, const uint16_t* k_lds, const uint16_t* v_lds, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    f32x4 sacc[4];
+  auto compute_tile = [&](int t, const uint16_t* k_lds, const uint16_t* v_lds) {
+    f32x4 sacc[RT][4];
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) sacc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) sacc[rt][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 6; ++c)
 #pragma unroll
-      for (int sub = 0; sub < 4; ++sub)
-        sacc[sub] = mfma_16x16x32(
-            *reinterpret_cast<const u32x4*>(k_lds + (sub * 16 + col) * kKLdsStride + 8 * grp + 32 * c),
-            qreg[c], sacc[sub]);
-
-    // sacc[sub][i] = raw score of key t*64 + sub*16 + 4*grp + i, row col.
-    float mx = -INFINITY;
+      for (int sub = 0; sub < 4; ++sub) {
+        const u32x4 kf =
+            *reinterpret_cast<const u32x4*>(k_lds + (sub * 16 + col) * kKLdsStride + 8 * grp + 32 * c);
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = sacc[sub][i];
-        if constexpr (MASKED) {
-          const int j = t * kTileKeys + sub * 16 + 4 * grp + i;
-          const bool vis = j >= lo_row && j <= hi_row;
-          x = vis ? x : -INFINITY;
-          sacc[sub][i] = x;
-          if constexpr (COUNT) cnt += vis ? 1 : 0;
-        } else {
-          if constexpr (COUNT) cnt += 1;
-        }
-        mx = fmaxf(mx, x);
+        for (int rt = 0; rt < RT; ++rt) sacc[rt][sub] = mfma_16x16x32(kf, qreg[rt][c], sacc[rt][sub]);
       }
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m, mx * scale);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    u32x2 pb[4];
+
+    // sacc[rt][sub][i] = raw score of key t*64 + sub*16 + 4*grp + i for this
+    // lane's row of row tile rt.  The mask branch is uniform over the
+    // workgroup.
+    if (has_pad || t * kTileKeys < lo_last || t * kTileKeys + kTileKeys - 1 > p_first) {
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      float pr[4];
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(__builtin_fmaf(sacc[sub][i], scale, -m_use));
-      pb[sub] = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+        for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = t * kTileKeys + sub * 16 + 4 * grp + i;
+            const bool vis = j >= lo_row[rt] && j <= hi_row[rt];
+            sacc[rt][sub][i] = vis ? sacc[rt][sub][i] : -INFINITY;
+            if constexpr (COUNT) cnt[rt] += vis ? 1 : 0;
+          }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        if constexpr (COUNT) cnt[rt] += 16;
     }
-    m = m_new;
-    if (__ballot(alpha != 1.f)) {
+    u32x4 pt[RT][2];
+    float alpha[RT];
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn) o[nn] *= alpha;
+    for (int rt = 0; rt < RT; ++rt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[rt][sub][i]);
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);
+      const float m_new = fmaxf(m[rt], mx * scale);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      alpha[rt] = fast_exp2(m[rt] - m_use);
+      u32x2 pb[4];
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(__builtin_fmaf(sacc[rt][sub][i], scale, -m_use));
+        pb[sub] = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+      }
+      pt[rt][0] = cat(pb[0], pb[1]);
+      pt[rt][1] = cat(pb[2], pb[3]);
+      m[rt] = m_new;
+      if (__ballot(alpha[rt] != 1.f)) {
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn) o[rt][nn] *= alpha[rt];
+      }
     }
 
     // O^T += V^T P^T over 32 keys per step: lane group grp contracts keys
@@ -177,18 +206,23 @@ void prefill_attn_kernel(const SplitArgs a) {
     // two transposing reads.  The row sums of this tile's (bf16) P come from
     // the matrix cores too: an all-ones V^T tile gives sum_k P[row][k] in
     // every element, across all four lane groups, with no shuffles.
-    f32x4 psum = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 psum[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) psum[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const u32x4 pt = cat(pb[2 * c], pb[2 * c + 1]);
       const uint16_t* vp = v_lds + (32 * c + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn)
-        o[nn] = mfma_16x16x32(cat(lds_read_tr16(vp + 16 * nn), lds_read_tr16(vp + 16 * kVLdsStride + 16 * nn)),
-                              pt, o[nn]);
-      psum = mfma_16x16x32(kOnesBf16x8, pt, psum);
+      for (int nn = 0; nn < 8; ++nn) {
+        const u32x4 vf = cat(lds_read_tr16(vp + 16 * nn), lds_read_tr16(vp + 16 * kVLdsStride + 16 * nn));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) o[rt][nn] = mfma_16x16x32(vf, pt[rt][c], o[rt][nn]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) psum[rt] = mfma_16x16x32(kOnesBf16x8, pt[rt][c], psum[rt]);
     }
-    l = __builtin_fmaf(l, alpha, psum[0]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) l[rt] = __builtin_fmaf(l[rt], alpha[rt], psum[rt][0]);
   };
 
   // Every stage step runs in every round so the loads keep one fixed order
@@ -200,11 +234,7 @@ void prefill_attn_kernel(const SplitArgs a) {
       const int t = t0 + i;
       uint16_t* cur = lds + (t & 1) * LDS_TILE;
       uint16_t* nxt = lds + ((t + 1) & 1) * LDS_TILE;
-      if (t < t_end) {
-        const bool whole = !has_pad && t * kTileKeys >= lo_last && t * kTileKeys + kTileKeys - 1 <= p_first;
-        if (whole) compute_tile(t, cur, cur + kKLdsElems, std::false_type{});
-        else compute_tile(t, cur, cur + kKLdsElems, std::true_type{});
-      }
+      if (t < t_end) compute_tile(t, cur, cur + kKLdsElems);
       // Widen tile t + 1 into the other buffer (its last readers passed the
       // barrier that ended the previous tile), then start loading t + 1 + NS.
       const int j = (i + 1) % NS;   // a constant once the loop is unrolled
@@ -215,31 +245,35 @@ void prefill_attn_kernel(const SplitArgs a) {
     }
   }
 
-  if constexpr (COUNT) {
-    cnt += __shfl_xor(cnt, 16, 64);
-    cnt += __shfl_xor(cnt, 32, 64);
-    if (row_ok && grp == 0 && a.count_out)
-      atomicAdd(a.count_out + (size_t)(r0 + tok) * a.hq + hh, cnt);
-  }
-  if (!row_ok) return;
-  const size_t out_row = (size_t)(r0 + tok) * a.hq + hh;
-  float coef;
-  if (a.sinks) {
-    const float s2 = a.sinks[hh] * kLog2e;
-    const float M2 = fmaxf(m, s2);
-    const float al = fast_exp2(m - M2);
-    coef = al / (l * al + fast_exp2(s2 - M2));
-  } else {
-    coef = 1.f / l;
-  }
-  coef *= a.v_scale;
-  uint16_t* op = a.out + out_row * kHeadDimV + 4 * grp;
 #pragma unroll
-  for (int nn = 0; nn < 8; ++nn) {
-    const f32x4 v = o[nn] * coef;
-    *reinterpret_cast<u32x2*>(op + 16 * nn) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  for (int rt = 0; rt < RT; ++rt) {
+    if constexpr (COUNT) {
+      int c = cnt[rt];
+      c += __shfl_xor(c, 16, 64);
+      c += __shfl_xor(c, 32, 64);
+      if (row_ok[rt] && grp == 0 && a.count_out)
+        atomicAdd(a.count_out + (size_t)(r0 + tok[rt]) * a.hq + hh[rt], c);
+    }
+    if (!row_ok[rt]) continue;
+    const size_t out_row = (size_t)(r0 + tok[rt]) * a.hq + hh[rt];
+    float coef;
+    if (a.sinks) {
+      const float s2 = a.sinks[hh[rt]] * kLog2e;
+      const float M2 = fmaxf(m[rt], s2);
+      const float al = fast_exp2(m[rt] - M2);
+      coef = al / (l[rt] * al + fast_exp2(s2 - M2));
+    } else {
+      coef = 1.f / l[rt];
+    }
+    coef *= a.v_scale;
+    uint16_t* op = a.out + out_row * kHeadDimV + 4 * grp;
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) {
+      const f32x4 v = o[rt][nn] * coef;
+      *reinterpret_cast<u32x2*>(op + 16 * nn) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+    if (a.lse_out && grp == 0) a.lse_out[out_row] = (m[rt] + log2f(l[rt])) * kLn2;
   }
-  if (a.lse_out && grp == 0) a.lse_out[out_row] = (m + log2f(l)) * kLn2;
 }
 
 }  // namespace diffkv
