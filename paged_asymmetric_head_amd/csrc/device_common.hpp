@@ -74,6 +74,29 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 
+// A register copy the compiler cannot look through.
+__device__ __forceinline__ uint32_t opaque_copy(uint32_t x) {
+  uint32_t y;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+  return y;
+}
+
+// Max over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48) on
+// the VALU, with gfx950's row swaps instead of LDS permutes.  Called with
+// both operands equal, v_permlane16_swap returns the values of the even and
+// the odd row of each row pair, v_permlane32_swap those of the low and the
+// high half-wave.  The second result goes through opaque_copy: without it
+// this compiler (ROCm 7.2 clang) replaces the second result by the first
+// once it is reinterpreted as a float, and the max silently disappears.
+__device__ __forceinline__ float max_over_lane_groups(float v) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  v = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, opaque_copy(a[1])));
+  const uint32_t y = __builtin_bit_cast(uint32_t, v);
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, opaque_copy(b[1])));
+}
+
 __device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

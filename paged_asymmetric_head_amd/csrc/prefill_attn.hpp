@@ -34,15 +34,21 @@ namespace diffkv {
 constexpr int kPfRowTiles = 2;                               // 16-row tiles per wave
 constexpr int kPfWaves = kPrefillRows / (16 * kPfRowTiles);  // waves per workgroup
 constexpr int kPfThreads = 64 * kPfWaves;
-#ifndef DIFFKV_PREFILL_STAGES
-#define DIFFKV_PREFILL_STAGES 2
+// Register stages of gathered tiles: two for FP8 (12 VGPRs each), one for
+// bf16, whose stages are twice as large and would not fit beside two row
+// tiles' accumulators at two waves per SIMD.
+#ifndef DIFFKV_PREFILL_STAGES_FP8
+#define DIFFKV_PREFILL_STAGES_FP8 2
+#endif
+#ifndef DIFFKV_PREFILL_STAGES_BF16
+#define DIFFKV_PREFILL_STAGES_BF16 1
 #endif
 
 template <bool FP8, bool UPAGE, bool COUNT>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_attn_kernel(const SplitArgs a) {
   using IO = KvTile<FP8, UPAGE, kPfThreads>;
-  constexpr int NS = DIFFKV_PREFILL_STAGES;
+  constexpr int NS = FP8 ? DIFFKV_PREFILL_STAGES_FP8 : DIFFKV_PREFILL_STAGES_BF16;
   constexpr int RT = kPfRowTiles;
   constexpr int LDS_TILE = kKLdsElems + kVLdsElems;
 
@@ -178,8 +184,7 @@ void prefill_attn_kernel(const SplitArgs a) {
       for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[rt][sub][i]);
-      mx = wave_max_xor(mx, 16);
-      mx = wave_max_xor(mx, 32);
+      mx = max_over_lane_groups(mx);
       const float m_new = fmaxf(m[rt], mx * scale);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       alpha[rt] = fast_exp2(m[rt] - m_use);

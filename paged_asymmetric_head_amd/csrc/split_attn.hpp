@@ -181,8 +181,7 @@ void split_attn_kernel(const SplitArgs a) {
     for (int sub = 0; sub < SUBS; ++sub)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[sub][i]);
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
+    mx = max_over_lane_groups(mx);
     const float m_new = fmaxf(m, mx * scale);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
