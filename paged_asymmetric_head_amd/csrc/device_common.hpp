@@ -52,6 +52,17 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Online-softmax reference point (base-2 logit domain).  A row keeps its
+// reference m while the tile max stays within kStaleMaxSlack of it, so the
+// unnormalised P = 2^(x - m) stays below 2^kStaleMaxSlack (well inside bf16
+// and fp32 range) and O, l need no rescale for most tiles; m, l and O stay
+// mutually consistent, so the normalised result is the same.  A row with no
+// visible key yet has m = -inf and takes the first finite max.
+constexpr float kStaleMaxSlack = 8.f;
+__device__ __forceinline__ float next_reference(float m, float tile_max) {
+  return tile_max > m + kStaleMaxSlack ? tile_max : m;
+}
+
 // Two fp32 -> two bf16 in one word, round to nearest even (one
 // v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

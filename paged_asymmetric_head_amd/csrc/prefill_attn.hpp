@@ -20,8 +20,9 @@
 // Only tiles that cross a row's causal or window boundary (or hold padding
 // rows) are masked; the others skip the compares.  The exp argument folds
 // the scale into one FMA on the raw score (the scale is positive), the row
-// sums of P come from an extra all-ones matrix-core tile, and the O rescale
-// is skipped when no row's running max moved.
+// sums of P come from an extra all-ones matrix-core tile, and a row's
+// reference max moves only when a tile's max exceeds it by more than 8 (a
+// factor 2^8 in P), so the O rescale is rare.
 // The whole key range of a row block runs in one workgroup: no split, no
 // merge; row blocks are issued latest-token first (they are the longest).
 #pragma once
@@ -185,7 +186,7 @@ void prefill_attn_kernel(const SplitArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[rt][sub][i]);
       mx = max_over_lane_groups(mx);
-      const float m_new = fmaxf(m[rt], mx * scale);
+      const float m_new = next_reference(m[rt], mx * scale);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       alpha[rt] = fast_exp2(m[rt] - m_use);
       u32x2 pb[4];

@@ -182,7 +182,7 @@ void split_attn_kernel(const SplitArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[sub][i]);
     mx = max_over_lane_groups(mx);
-    const float m_new = fmaxf(m, mx * scale);
+    const float m_new = next_reference(m, mx * scale);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
     u32x2 pb[SUBS];
