@@ -70,6 +70,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// Two bf16 codes in one word (low half first) -> two floats, exactly.
+__device__ __forceinline__ f32x2 unpack_bf16x2(uint32_t w) {
+  return f32x2{__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xFFFF0000u)};
+}
+
 // Four OCP E4M3FN codes (one 32-bit word, byte 0 first) -> four bf16 codes in
 // two words, with gfx950's packed converter at scale 1.0.  Every finite
 // E4M3 value has at most 4 significant bits and an exponent in [-9, 8], so

@@ -204,7 +204,7 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
   a.lse_out = lse_out;
   a.count_out = count_out;
   if (plan.num_splits > 1) {
-    a.part_o = static_cast<float*>(workspace);
+    a.part_o = static_cast<uint16_t*>(workspace);
     a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           ((plan.part_o_bytes + 255) / 256) * 256);
   }

@@ -101,7 +101,7 @@ inline SplitPlan plan_split(const diffkv_attn_desc& d, int window, bool allow_sp
   p.num_splits = s;
   if (s > 1) {
     const size_t prow = (size_t)pairs * s * p.rows;
-    p.part_o_bytes = prow * kHeadDimV * sizeof(float);
+    p.part_o_bytes = prow * kHeadDimV * sizeof(uint16_t);   // bf16 partial rows
     p.part_lse_bytes = prow * sizeof(float);
     p.workspace_bytes = ((p.part_o_bytes + 255) / 256) * 256 + ((p.part_lse_bytes + 255) / 256) * 256;
   }

@@ -38,8 +38,8 @@ struct SplitArgs {
   const int32_t* seq_lens;
   const int32_t* q_lens;
   const float* sinks;
-  float* part_o;
-  float* part_lse;
+  uint16_t* part_o;     // bf16 normalised partial rows [.., 128]
+  float* part_lse;      // base-2 log-sum-exp of each partial row
   uint16_t* out;
   float* lse_out;
   int32_t* count_out;
@@ -313,10 +313,15 @@ void split_attn_kernel(const SplitArgs a) {
     if (a.lse_out && grp == 0) a.lse_out[out_row] = (m + log2f(l)) * kLn2;
   } else {
     const size_t prow = (((size_t)bg * a.n_qtiles + qt) * a.num_splits + s) * ROWS + rt * 16 + col;
+    // Partial rows are normalised (a convex combination of V rows), so bf16
+    // keeps fp32's range; its rounding matches the output's own.
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* pp = a.part_o + prow * kHeadDimV + 4 * grp;
+    uint16_t* pp = a.part_o + prow * kHeadDimV + 4 * grp;
 #pragma unroll
-    for (int nn = 0; nn < 8; ++nn) *reinterpret_cast<f32x4*>(pp + 16 * nn) = o[nn] * inv;
+    for (int nn = 0; nn < 8; ++nn) {
+      const f32x4 v = o[nn] * inv;
+      *reinterpret_cast<u32x2*>(pp + 16 * nn) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
     if (grp == 0) a.part_lse[prow] = l > 0.f ? m + log2f(l) : -INFINITY;
   }
 }
@@ -359,11 +364,11 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const SplitArgs a) {
   for (int s0 = 0; s0 < S; s0 += 64) {
     const int cnt = min(64, S - s0);
     const float lse_l = lane < cnt ? a.part_lse[prow0 + (size_t)(s0 + lane) * ROWS] : -INFINITY;
-    const float* po = a.part_o + (prow0 + (size_t)s0 * ROWS) * kHeadDimV + 2 * lane;
-    f32x2 v[16];
+    const uint16_t* po = a.part_o + (prow0 + (size_t)s0 * ROWS) * kHeadDimV + 2 * lane;
+    uint32_t raw[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k)
-      v[k] = *reinterpret_cast<const f32x2*>(po + (size_t)min(wave + 4 * k, cnt - 1) * ROWS * kHeadDimV);
+      raw[k] = *reinterpret_cast<const uint32_t*>(po + (size_t)min(wave + 4 * k, cnt - 1) * ROWS * kHeadDimV);
     const float m_new = fmaxf(m_run, wave_max_all(lse_l));
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float f = fast_exp2(m_run - m_use);
@@ -375,7 +380,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const SplitArgs a) {
     for (int k = 0; k < 16; ++k) {
       const int i = wave + 4 * k;
       const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), min(i, 63)));
-      if (i < cnt && w > 0.f) acc += w * v[k];
+      if (i < cnt && w > 0.f) acc += w * unpack_bf16x2(raw[k]);
     }
     m_run = m_new;
   }
