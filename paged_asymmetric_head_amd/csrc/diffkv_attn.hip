@@ -188,7 +188,7 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
     return e == hipSuccess ? DIFFKV_OK : DIFFKV_HIP_ERROR;
   }
 
-  const SplitPlan plan = plan_split(*d, window, true, split_wgs_per_cu(fp8, upage));
+  const SplitPlan plan = plan_split(*d, window, true, kSplitWavesPerEu);
   if (plan.num_splits > 1 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
     return DIFFKV_WORKSPACE_TOO_SMALL;
 
@@ -280,8 +280,7 @@ int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry) {
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window) {
   if (validate_desc(desc, entry) != DIFFKV_OK) return 0;
   if (entry == DIFFKV_ENTRY_PREFILL) return 1;
-  return plan_split(*desc, window, true,
-                    split_wgs_per_cu(desc->kv_dtype == DIFFKV_KV_FP8_E4M3, desc->page_size >= kTileKeys))
+  return plan_split(*desc, window, true, kSplitWavesPerEu)
       .num_splits;
 }
 

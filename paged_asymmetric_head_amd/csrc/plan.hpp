@@ -45,26 +45,24 @@ inline long long max_keys_bound(const diffkv_attn_desc& d, int window) {
 }
 
 // Register stages of the split kernel (tiles of K/V in flight per
-// workgroup) and the workgroups that stay resident per CU with them
-// (bf16 stages are twice as large, so fewer workgroups fit).
-// Register stages of the split kernel (tiles of K/V in flight per
-// workgroup) and the waves per SIMD it is compiled for.  With pages of at
-// least one tile the block-table lookups are scalar and two workgroups fit a
-// CU; smaller pages keep per-lane page ids and fit one.
+// workgroup, beyond the one in LDS) and the waves per SIMD it is compiled
+// for, which is also the number of its 256-thread workgroups resident per
+// CU.  Both K/V formats keep a single register stage: with a resident round
+// of workgroups that is enough loads in flight for HBM, and deeper stages
+// measured slower (the opening burst of loads delays every workgroup's
+// first tile).  Two workgroups per CU for every page size (three measured no
+// better).
 #ifndef DIFFKV_BF16_STAGES
-#define DIFFKV_BF16_STAGES 2
+#define DIFFKV_BF16_STAGES 1
 #endif
 #ifndef DIFFKV_FP8_STAGES
-#define DIFFKV_FP8_STAGES 4
+#define DIFFKV_FP8_STAGES 1
 #endif
-#ifndef DIFFKV_UPAGE_WAVES_PER_EU
-#define DIFFKV_UPAGE_WAVES_PER_EU 2
+#ifndef DIFFKV_SPLIT_WAVES_PER_EU
+#define DIFFKV_SPLIT_WAVES_PER_EU 2
 #endif
 template <bool FP8> constexpr int kSplitStages = FP8 ? DIFFKV_FP8_STAGES : DIFFKV_BF16_STAGES;
-constexpr int split_waves_per_eu(bool /*fp8*/, bool upage) {
-  return upage ? DIFFKV_UPAGE_WAVES_PER_EU : 1;
-}
-inline int split_wgs_per_cu(bool fp8, bool upage) { return split_waves_per_eu(fp8, upage); }
+constexpr int kSplitWavesPerEu = DIFFKV_SPLIT_WAVES_PER_EU;
 
 // Split count: one resident round of workgroups over the 256 CUs (a second
 // round would pay the start-up chain seq_lens -> block table -> data again),

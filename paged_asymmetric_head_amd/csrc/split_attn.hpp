@@ -62,7 +62,7 @@ __device__ __forceinline__ void split_tiles(int kv_lo, int kv_hi, int S, int s, 
 }
 
 template <bool FP8, int RT, bool DIRECT, bool COUNT, bool UPAGE, int NS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(split_waves_per_eu(FP8, UPAGE), 8)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSplitWavesPerEu, 8)))
 void split_attn_kernel(const SplitArgs a) {
   constexpr int ROWS = 16 * RT;
   constexpr int KW = 4 / RT;                 // waves splitting the keys of one row tile
