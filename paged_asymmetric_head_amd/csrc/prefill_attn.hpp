@@ -35,11 +35,11 @@ namespace diffkv {
 constexpr int kPfRowTiles = 2;                               // 16-row tiles per wave
 constexpr int kPfWaves = kPrefillRows / (16 * kPfRowTiles);  // waves per workgroup
 constexpr int kPfThreads = 64 * kPfWaves;
-// Register stages of gathered tiles: two for FP8 (12 VGPRs each), one for
-// bf16, whose stages are twice as large and would not fit beside two row
-// tiles' accumulators at two waves per SIMD.
+// Register stages of gathered tiles beyond the two LDS buffers: one for
+// both formats (two measured the same for FP8 and spill for bf16 beside two
+// row tiles' accumulators at two waves per SIMD).
 #ifndef DIFFKV_PREFILL_STAGES_FP8
-#define DIFFKV_PREFILL_STAGES_FP8 2
+#define DIFFKV_PREFILL_STAGES_FP8 1
 #endif
 #ifndef DIFFKV_PREFILL_STAGES_BF16
 #define DIFFKV_PREFILL_STAGES_BF16 1
