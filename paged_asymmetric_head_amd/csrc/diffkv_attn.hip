@@ -103,12 +103,23 @@ hipError_t dispatch_split(const SplitArgs& a, int rt, bool upage, dim3 grid, boo
   }
 }
 
+// Merge shape by split count: one wave when its loads cover every split
+// (16 or 32), else four waves covering 128 splits per pass.
+template <int ROWS>
+const void* merge_kernel_for(int splits, int& threads) {
+  if (splits <= 16) { threads = 64; return reinterpret_cast<const void*>(&split_merge_kernel<ROWS, 1, 16>); }
+  if (splits <= 32) { threads = 64; return reinterpret_cast<const void*>(&split_merge_kernel<ROWS, 1, 32>); }
+  threads = 256;
+  return reinterpret_cast<const void*>(&split_merge_kernel<ROWS, 4, 32>);
+}
+
 hipError_t launch_merge(const SplitArgs& a, int rows, dim3 grid, hipStream_t stream) {
   void* args[] = {const_cast<SplitArgs*>(&a)};
-  const void* fn = rows == 16 ? reinterpret_cast<const void*>(&split_merge_kernel<16>)
-                 : rows == 32 ? reinterpret_cast<const void*>(&split_merge_kernel<32>)
-                              : reinterpret_cast<const void*>(&split_merge_kernel<64>);
-  return hipLaunchKernel(fn, grid, dim3(256), args, 0, stream);
+  int threads = 0;
+  const void* fn = rows == 16 ? merge_kernel_for<16>(a.num_splits, threads)
+                 : rows == 32 ? merge_kernel_for<32>(a.num_splits, threads)
+                              : merge_kernel_for<64>(a.num_splits, threads);
+  return hipLaunchKernel(fn, grid, dim3(threads), args, 0, stream);
 }
 
 template <bool FP8, bool UPAGE, bool COUNT>

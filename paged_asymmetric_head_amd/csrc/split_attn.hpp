@@ -338,16 +338,19 @@ __device__ __forceinline__ float wave_sum_all(float v) {
 }
 
 // Combines the split partials of one query row: weights 2^(lse_s - M), the
-// sink joining the denominator, v_scale, bf16 store.  One 256-thread
-// workgroup per row.  Every split wrote its row (an empty split an lse of
-// -inf), so the lse values and the partial rows are all loaded at once, with
-// no dependence on the sequence lengths: per group of 64 splits each lane
-// reads one lse and wave w the partial rows of splits w, w+4, ... (two output
-// dims per lane).  Groups are combined with a running maximum; the four
-// waves' sums meet in LDS in a fixed order (deterministic).
-template <int ROWS>
-__global__ __launch_bounds__(256) void split_merge_kernel(const SplitArgs a) {
-  __shared__ f32x2 red[3][64];
+// sink joining the denominator, v_scale, bf16 store.  One workgroup of W
+// waves per row.  Every split wrote its row (an empty split an lse of -inf),
+// so a pass over up to W*K splits issues all of its loads before any
+// arithmetic: every wave reads all the pass's lse values (so each has the
+// pass max and the weight sum), wave w the partial rows of splits
+// w, w+W, ..., two output dims per lane.  Passes combine with a running
+// maximum; the waves' sums meet in LDS in a fixed order (deterministic).
+// One wave (no LDS, no barrier) when the splits fit its K loads.
+template <int ROWS, int W, int K>
+__global__ __launch_bounds__(64 * W) void split_merge_kernel(const SplitArgs a) {
+  constexpr int PASS = W * K;               // splits per pass
+  constexpr int LI = (PASS + 63) / 64;      // lse values per lane per pass
+  __shared__ f32x2 red[W > 1 ? W - 1 : 1][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int R = blockIdx.x;                 // row of this (sequence, KV head)
   const int qt = R / ROWS, r = R % ROWS;
@@ -359,37 +362,57 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const SplitArgs a) {
   const int r0 = seq_row_start(a.q_lens, b);
 
   const size_t prow0 = ((size_t)bg * a.n_qtiles + qt) * S * ROWS + r;
+  const uint16_t* po0 = a.part_o + prow0 * kHeadDimV + 2 * lane;
   float m_run = -INFINITY, ksum = 0.f;
   f32x2 acc = f32x2{0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    const int cnt = min(64, S - s0);
-    const float lse_l = lane < cnt ? a.part_lse[prow0 + (size_t)(s0 + lane) * ROWS] : -INFINITY;
-    const uint16_t* po = a.part_o + (prow0 + (size_t)s0 * ROWS) * kHeadDimV + 2 * lane;
-    uint32_t raw[16];
+  for (int s0 = 0; s0 < S; s0 += PASS) {
+    float lse_l[LI];
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
-      raw[k] = *reinterpret_cast<const uint32_t*>(po + (size_t)min(wave + 4 * k, cnt - 1) * ROWS * kHeadDimV);
-    const float m_new = fmaxf(m_run, wave_max_all(lse_l));
+    for (int i = 0; i < LI; ++i) {
+      const int j = s0 + lane + 64 * i;
+      lse_l[i] = j < S ? a.part_lse[prow0 + (size_t)j * ROWS] : -INFINITY;
+    }
+    uint32_t raw[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int j = min(s0 + wave + W * k, S - 1);
+      raw[k] = *reinterpret_cast<const uint32_t*>(po0 + (size_t)j * ROWS * kHeadDimV);
+    }
+    float mx = lse_l[0];
+#pragma unroll
+    for (int i = 1; i < LI; ++i) mx = fmaxf(mx, lse_l[i]);
+    const float m_new = fmaxf(m_run, wave_max_all(mx));
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float f = fast_exp2(m_run - m_use);
     acc *= f;
     ksum *= f;
-    const float wl = fast_exp2(lse_l - m_use);
-    ksum += wl;
+    float wl[LI];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int i = wave + 4 * k;
-      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), min(i, 63)));
-      if (i < cnt && w > 0.f) acc += w * unpack_bf16x2(raw[k]);
+    for (int i = 0; i < LI; ++i) {
+      wl[i] = fast_exp2(lse_l[i] - m_use);
+      ksum += wl[i];
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int i = wave + W * k;           // split within the pass (wave-uniform)
+      float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl[0]), i & 63));
+#pragma unroll
+      for (int li = 1; li < LI; ++li) {
+        const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl[li]), i & 63));
+        w = (i >> 6) == li ? wi : w;
+      }
+      if (s0 + i < S && w > 0.f) acc += w * unpack_bf16x2(raw[k]);
     }
     m_run = m_new;
   }
-  if (wave > 0) red[wave - 1][lane] = acc;
-  __syncthreads();
-  if (wave > 0 || R >= n * G) return;
-  acc += red[0][lane];
-  acc += red[1][lane];
-  acc += red[2][lane];
+  if constexpr (W > 1) {
+    if (wave > 0) red[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < W - 1; ++w) acc += red[w][lane];
+  }
+  if (R >= n * G) return;
   ksum = wave_sum_all(ksum);
   const int tok = R / G, h = g * G + R % G;
   const float s2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;

@@ -100,7 +100,7 @@ def test_grid_all_entries(case):
         compare(to_np(o), to_np(outs[0]), "cross-entry")
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 7, 40])
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 20, 40, 200])
 def test_forced_split_counts(splits):
     inp = make_paged_inputs(77, seq_lens=[3000, 1777, 90], q_lens=[8, 5, 3], num_q_heads=8,
                             num_kv_heads=1, page_size=16, kv_dtype="bf16", sinks=True)
