@@ -100,7 +100,9 @@ typedef struct diffkv_attn_desc {
  *   softmax_scale     multiplies q.k before the softmax
  *   out          bf16  [total_q, Hq, 128], written (round to nearest even)
  *   lse_out      fp32  [total_q, Hq] natural-log log-sum-exp of the key
- *                logits (sink excluded), or NULL
+ *                logits (sink excluded), or NULL; the row sums behind it
+ *                add the bf16-rounded probabilities the P.V product uses,
+ *                so it is exact to about 2^-8
  *   count_out    int32 [total_q, Hq]: number of keys each row combined, or
  *                NULL (a check on which slots are read; costs time)
  *   workspace    device scratch of at least diffkv_attn_workspace_bytes(desc,

@@ -4,12 +4,11 @@
 // K and V live in two caches because their rows differ in width
 // ("sglang PR 32818, Route asymmetric-KV models to fa4 on SM100"); FP8 E4M3
 // rows are widened to bf16 on the way into LDS ("diffbot/MiMo-V2.6-Flash-RL-
-// FP8KV-W4A8-2x-RTX-PRO-6000", What the kernels do).  A workgroup of 256
-// threads moves a tile as 16-byte units, consecutive lanes on consecutive
-// pieces of a row, through registers: the caller keeps several tiles' loads
-// in flight (`Stage`s) and writes the oldest into LDS.  NT threads share a
-// tile (256 or 512); when they do not divide it evenly, whole waves take one
-// unit fewer.
+// FP8KV-W4A8-2x-RTX-PRO-6000", What the kernels do).  A workgroup of NT
+// threads (256 or 512) moves a tile as 16-byte units, consecutive lanes on
+// consecutive pieces of a row, through registers: the caller keeps the next
+// tiles' loads in flight (`Stage`s) and writes the oldest into LDS.  When
+// the threads do not divide the tile evenly, whole waves take one unit fewer.
 #pragma once
 
 #include "device_common.hpp"

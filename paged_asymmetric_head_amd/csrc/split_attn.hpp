@@ -1,7 +1,7 @@
 // Split-KV paged attention for decode and speculative verify on gfx950, plus
 // the log-sum-exp merge of the split partials.
 //
-// Work decomposition ("diffkv/MiMo-V2.6-Flash-RL-FP8KV-W4A8-2x-RTX-PRO-6000",
+// Work decomposition ("diffbot/MiMo-V2.6-Flash-RL-FP8KV-W4A8-2x-RTX-PRO-6000",
 // What the kernels do: without split-KV a multi-token verify ran on a handful
 // of workgroups; split-KV fixed that): one workgroup per (key split, query
 // tile, sequence * KV head).  A query tile is up to 64 rows; row r of a
@@ -10,16 +10,17 @@
 // program per whole verify, same page).
 //
 // Per 64-key tile the workgroup gathers K (192 wide) and V (128 wide) rows
-// through the block table with 16-byte loads, converts FP8 E4M3 to bf16 on
-// the way into LDS, and stores V transposed so it can feed the matrix cores.
-// Each wave owns one 16-row query tile and a quarter, half or all of the 64
-// keys (4, 2 or 1 row tiles per workgroup) and runs
+// through the block table with 16-byte loads and writes them row-major into
+// LDS as bf16 (FP8 E4M3 widened on the way).  Each wave owns one 16-row
+// query tile and a quarter, half or all of the 64 keys (4, 2 or 1 row tiles
+// per workgroup) and runs
 //   S^T = K * Q^T        (v_mfma_f32_16x16x32_bf16, 6 steps over 192 dims)
 //   mask -> online softmax in base 2 (rows live in lanes, keys across the
-//           4 lane groups: two xor-shuffles per reduction)
+//           4 lane groups: a row max is two lane-row swaps on the VALU)
 //   O^T += V^T * P^T     (v_mfma_f32_16x16x32_bf16 when a wave holds 32 or
 //                         more keys of the tile, else 16x16x16; 8 tiles over
-//                         the 128 dims)
+//                         the 128 dims; V^T comes from transposing LDS reads
+//                         of the row-major V tile)
 // Keeping S and O transposed puts one query row in each lane, so the softmax
 // rescale needs no data movement between lanes.
 // The global loads of the next NS tiles are in flight in registers while a
