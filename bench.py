@@ -26,6 +26,7 @@ calls has the library's dispatch stamp each main kernel with HIP events
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import math
 import os
@@ -112,13 +113,33 @@ def algorithmic_work(inp):
     return {"kv_bytes": kv_bytes, "pairs": pairs, "flops": 640 * pairs, "q_ctx": qctx}
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/|\s+', re.S)
+
+
+def _code_only(text):
+    """C++ source with comments dropped and whitespace runs collapsed
+    (string and character literals kept), so editing a comment does not
+    count as a kernel change."""
+    def keep(m):
+        t = m.group(0)
+        return " " if t.startswith("//") or t.startswith("/*") or t.isspace() else t
+    return re.sub(r"\s+", " ", _CODE_TOKENS.sub(keep, text)).strip()
+
+
 def kernel_source_sha():
+    """Identifies the kernels the counters were taken on: the code of the HIP
+    sources and the public header, and the compile flags."""
     import glob
+    from paged_asymmetric_head_amd.build import command
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(ROOT, "paged_asymmetric_head_amd", "csrc", "*"))):
-        with open(path, "rb") as f:
+    paths = sorted(glob.glob(os.path.join(ROOT, "paged_asymmetric_head_amd", "csrc", "*")))
+    paths.append(os.path.join(ROOT, "include", "diffkv_attn.h"))
+    for path in paths:
+        with open(path, encoding="utf-8") as f:
             h.update(os.path.basename(path).encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
+    flags = [c for c in command("OUT") if not os.path.isabs(c) and c != "OUT" and "hipcc" not in c]
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 
