@@ -15,13 +15,18 @@ What it follows (the web pages this project is built from):
   * "sglang PR 32818, Route asymmetric-KV models to fa4 on SM100": K and V
     live in separate paged caches because their row widths differ.
 
+It also holds the paged KV write (kv_write.py): the new tokens' rows stored
+into their slots, FP8 encoding from the format's definition.
+
 Every function computes a plain definition in float64; no blocking or fusion
 beyond what the definition states.  Pinned by the CPU tests against brute
 force, a library attention routine, closed forms and invariants; the only
 unpinned part is noted in `attention.py`.
 """
 
-from .codecs import decode_bf16, decode_e4m3fn
+from .codecs import decode_bf16, decode_e4m3fn, encode_e4m3fn
 from .attention import paged_attention, OracleResult
+from .kv_write import paged_kv_write
 
-__all__ = ["decode_bf16", "decode_e4m3fn", "paged_attention", "OracleResult"]
+__all__ = ["decode_bf16", "decode_e4m3fn", "encode_e4m3fn", "paged_attention", "OracleResult",
+           "paged_kv_write"]

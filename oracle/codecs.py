@@ -11,6 +11,9 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
   finite magnitude is 2^8 * 1.75 = 448.  The FP8 KV cache on the
   "diffbot/MiMo-V2.6-Flash-RL-FP8KV-W4A8-2x-RTX-PRO-6000" page (intro and
   "What the kernels do") stores this format.
+
+encode_e4m3fn is the plain definition of round-to-nearest-even onto the
+finite E4M3FN values, after clamping the magnitude to 448.
 """
 
 import numpy as np
@@ -34,3 +37,38 @@ def decode_e4m3fn(codes):
     mag = np.where(e > 0, normal, subnormal)
     out = sign * mag
     return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+# The 127 non-negative finite E4M3FN values, in code order (ascending).
+_E4M3_GRID = None
+
+
+def encode_e4m3fn(x):
+    """float32 array -> OCP E4M3FN codes (uint8): round to nearest even.
+
+    Magnitudes above 448 (infinity included) clamp to 448; NaN maps to the
+    NaN code 0x7F with the input's sign bit.  The nearest of the finite
+    values is chosen; on a tie the even code wins, which is the even
+    mantissa, since consecutive codes are consecutive values and a code's
+    last bit is its mantissa's last bit.  The sign bit is copied (so -0.0
+    encodes as 0x80).
+    """
+    global _E4M3_GRID
+    if _E4M3_GRID is None:
+        _E4M3_GRID = decode_e4m3fn(np.arange(127, dtype=np.uint8))
+    grid = _E4M3_GRID
+    v = np.asarray(x, dtype=np.float32)
+    sign = np.signbit(v).astype(np.uint8) << np.uint8(7)
+    a = np.abs(v.astype(np.float64))
+    nan = np.isnan(a)
+    a = np.where(nan, 0.0, np.minimum(a, 448.0))
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 0, 126)     # first value >= a
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo = a - grid[lo]
+    d_hi = grid[hi] - a
+    pick = np.where(d_hi < d_lo, hi, lo)
+    tie = (d_hi == d_lo) & (hi != lo)
+    pick = np.where(tie, np.where(hi % 2 == 0, hi, lo), pick)
+    pick = np.where(a == grid[hi], hi, pick)                          # exact values
+    codes = pick.astype(np.uint8) | sign
+    return np.where(nan, np.uint8(0x7F) | sign, codes).astype(np.uint8)
