@@ -20,7 +20,8 @@ steps alone (HIP events around the K calls, no per-call instrumentation).
 calls has the library's dispatch stamp each main kernel with HIP events
 (diffkv_attn_profile_next_call); their mean is the kernel's duration.
 `cpu_baseline` times the FP64 oracle on the host on a bounded sample.
-`extra` carries the other workloads measured the same way.
+`extra` carries the other workloads measured the same way, and the paged KV
+write (diffkv_kv_write) on the decode and prefill token counts.
 """
 
 import argparse
@@ -157,6 +158,36 @@ def measured_traffic(workload, sha):
     return rec.get("bytes_per_launch")
 
 
+def time_calls(calls, steps, warmup, events, stream):
+    """Warm up, then time exactly `steps` calls (rotating over `calls`) with a
+    pair of HIP events around them; a second pass of the same calls has the
+    library stamp each main kernel's dispatch with its own pair of events.
+    Returns (total ms, wall seconds, sorted per-kernel ms)."""
+    import torch
+    from paged_asymmetric_head_amd import binding as B
+    n = len(calls)
+    pairs = [(events.create(), events.create()) for _ in range(steps)]
+    t0, t1 = events.create(), events.create()
+    for i in range(warmup):
+        calls[i % n]()
+    torch.cuda.synchronize()
+    # Timed region: exactly `steps` calls, nothing else on the stream.
+    wall0 = time.perf_counter()
+    events.record(t0, stream)
+    for k in range(steps):
+        calls[k % n]()
+    events.record(t1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = events.elapsed_ms(t0, t1)
+    for k in range(steps):
+        B.diffkv_attn_profile_next_call(pairs[k][0], pairs[k][1])
+        calls[k % n]()
+    torch.cuda.synchronize()
+    kern = sorted(events.elapsed_ms(a, b) for a, b in pairs)
+    return total_ms, wall, kern
+
+
 def measure(name, steps, warmup, events, target_bytes=1 << 30):
     import torch
     from paged_asymmetric_head_amd import binding as B
@@ -172,28 +203,7 @@ def measure(name, steps, warmup, events, target_bytes=1 << 30):
                                              for _ in range(layers - 1)]
     stream = torch.cuda.current_stream().cuda_stream
     calls = [dev.prepare(entry, k_cache=k, v_cache=v, stream=stream) for k, v in caches]
-    pairs = [(events.create(), events.create()) for _ in range(steps)]
-    t0, t1 = events.create(), events.create()
-
-    for i in range(warmup):
-        calls[i % layers]()
-    torch.cuda.synchronize()
-    # Timed region: exactly `steps` calls, nothing else on the stream.
-    wall0 = time.perf_counter()
-    events.record(t0, stream)
-    for k in range(steps):
-        calls[k % layers]()
-    events.record(t1, stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = events.elapsed_ms(t0, t1)
-    # Second pass, same calls: the library stamps each main kernel's dispatch
-    # with a pair of events, giving that kernel's own duration.
-    for k in range(steps):
-        B.diffkv_attn_profile_next_call(pairs[k][0], pairs[k][1])
-        calls[k % layers]()
-    torch.cuda.synchronize()
-    kern = sorted(events.elapsed_ms(a, b) for a, b in pairs)
+    total_ms, wall, kern = time_calls(calls, steps, warmup, events, stream)
     out = calls[(steps - 1) % layers].out
     if not bool(torch.isfinite(out.float()).all()):
         raise RuntimeError(f"{name}: non-finite output")
@@ -206,6 +216,53 @@ def measure(name, steps, warmup, events, target_bytes=1 << 30):
         "kernel_ms_mean": sum(kern) / len(kern), "kernel_ms_median": kern[len(kern) // 2],
         "work": work,
     }
+
+
+# Paged KV write, measured on the token counts of two attention workloads:
+# one new token per sequence (batched decode, bf16 cache) and a 4096-token
+# chunk (chunked prefill, FP8 cache).
+KV_WRITE_OF = {"kv_write_decode": "batched_decode", "kv_write_prefill": "chunked_prefill"}
+
+
+def measure_kv_write(name, steps, warmup, events, target_bytes=1 << 30):
+    """Time diffkv_kv_write; the algorithmic bytes are the bf16 rows read and
+    the cache rows written (K 192 + V 128 values per token and KV head)."""
+    import numpy as np
+    import torch
+    from paged_asymmetric_head_amd import binding as B
+    from paged_asymmetric_head_amd.device import DeviceInputs, _to_device
+    from paged_asymmetric_head_amd.synth import to_bf16_bits, workload
+
+    inp = workload(KV_WRITE_OF[name])
+    dev = DeviceInputs(inp)
+    decode = inp.max_q_len == 1
+    T, H = inp.total_q, inp.num_kv_heads
+    rng = np.random.default_rng(2)
+    pool = dev.k_cache.numel() * dev.k_cache.element_size() + dev.v_cache.numel() * dev.v_cache.element_size()
+    layers = max(1, min(16, math.ceil(target_bytes / pool)))
+    news = [(_to_device(to_bf16_bits(rng.standard_normal((T, H, 192), dtype=np.float32)), "cuda"),
+             _to_device(to_bf16_bits(rng.standard_normal((T, H, 128), dtype=np.float32)), "cuda"))
+            for _ in range(layers)]
+    caches = [(dev.k_cache, dev.v_cache)] + [(dev.k_cache.clone(), dev.v_cache.clone())
+                                             for _ in range(layers - 1)]
+    stream = torch.cuda.current_stream().cuda_stream
+    d = dev.desc("decode" if decode else "prefill")
+    calls = [B.prepared_kv_write(d, kn, vn, kc, vc, dev.block_table, dev.seq_lens,
+                                 None if decode else dev.q_lens, inp.k_scale, inp.v_scale, stream)
+             for (kn, vn), (kc, vc) in zip(news, caches)]
+    total_ms, wall, kern = time_calls(calls, steps, warmup, events, stream)
+    esize = 1 if inp.kv_dtype == "fp8" else 2
+    nbytes = T * H * (192 + 128) * (2 + esize)
+    ms = sum(kern) / len(kern)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    step_ms = total_ms / steps
+    return {"entry": "kv_write", "tokens": T, "num_kv_heads": H, "kv_dtype": inp.kv_dtype,
+            "page_size": inp.page_size, "ms_per_step": round(step_ms, 5),
+            "gbs": round(nbytes / (step_ms * 1e-3) / 1e9, 1), "layers": layers,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": None, "kernel": "kv_write_kernel", "kernel_ms": round(ms, 5),
+                         "work_per_launch": nbytes}}
 
 
 COPY_BYTES = 256 << 20
@@ -396,6 +453,10 @@ def main():
             mo = measure(other, args.extra_steps, 5, events)
             extra[other] = summary(mo, sha, other)
             del mo
+            torch.cuda.empty_cache()
+        for other in KV_WRITE_OF:
+            print(f"[bench] {other}: generating and measuring", file=sys.stderr, flush=True)
+            extra[other] = measure_kv_write(other, args.extra_steps, 5, events)
             torch.cuda.empty_cache()
         result["extra"] = extra
     if args.copy_calibration:

@@ -151,6 +151,40 @@ int diffkv_attn_prefill(const diffkv_attn_desc* desc, const void* q, const void*
                         int32_t* count_out, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
+/*
+ * Paged KV write: stores the new tokens' K and V rows into their cache slots,
+ * the step before attention reads them ("diffbot/MiMo-V2.6-Flash-RL-FP8KV-
+ * W4A8-2x-RTX-PRO-6000", intro: an E4M3 KV cache with per-tensor scales;
+ * "sglang PR 32818": K and V in two caches of different row widths).
+ *
+ *   k_new        bf16 [total_q, Hkv, 192], packed by sequence like q above
+ *   v_new        bf16 [total_q, Hkv, 128]
+ *   k_cache, v_cache, block_table, seq_lens, q_lens: as for attention (the
+ *                same descriptor serves both calls; num_q_heads is checked
+ *                but not used)
+ *   k_scale, v_scale  FP8 caches only: finite and > 0, else
+ *                DIFFKV_INVALID_ARGUMENT; ignored for bf16 caches
+ *
+ * New token i of sequence b (position p = seq_lens[b] - q_lens[b] + i) goes
+ * to slot p % P of page block_table[b][p / P], for every KV head.  A bf16
+ * cache receives the rows bit for bit.  An FP8 cache receives, per value x,
+ * the E4M3FN code of the fp32 quotient x / scale (correctly rounded
+ * division), clamped to +-448 and rounded to nearest even; NaN becomes 0x7F
+ * with the sign of the input, -0 becomes 0x80.  No other byte of either
+ * cache changes.
+ *
+ * Same ownership and data preconditions as attention (the call only writes
+ * the caches).  If two new tokens map to the same slot, which write lands is
+ * unspecified.  Unlike the attention calls, a token whose position is
+ * negative, whose page lies past block_table_stride or outside
+ * [0, num_pages), or whose packed row is not below total_q, is skipped:
+ * nothing is written for it.
+ */
+int diffkv_kv_write(const diffkv_attn_desc* desc, const void* k_new, const void* v_new,
+                    void* k_cache, void* v_cache, const int32_t* block_table,
+                    const int32_t* seq_lens, const int32_t* q_lens, float k_scale, float v_scale,
+                    hipStream_t stream);
+
 /* Bytes of workspace the entry needs for this descriptor (0 when none).
  * Host only; depends on the descriptor alone.  Returns 0 for an invalid
  * descriptor (check diffkv_attn_validate). */
@@ -164,8 +198,8 @@ int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry);
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window);
 
 /* Profiling hook.  Arms two caller-created HIP events for the next
- * decode/verify/prefill call made on this host thread: that call's main
- * attention kernel (not the split merge) is dispatched with them as its
+ * decode/verify/prefill/kv_write call made on this host thread: that call's
+ * main kernel (not the split merge) is dispatched with them as its
  * start and stop events (hipExtLaunchKernel), so hipEventElapsedTime(start,
  * stop) is that kernel's execution time.  The hook disarms after one call;
  * passing two NULLs disarms it.  Returns DIFFKV_INVALID_ARGUMENT if exactly

@@ -52,6 +52,9 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = _ENTRY_ARGS
         fn.restype = ctypes.c_int
+    lib.diffkv_kv_write.argtypes = [ctypes.POINTER(AttnDesc)] + [ctypes.c_void_p] * 7 + [
+        ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+    lib.diffkv_kv_write.restype = ctypes.c_int
     lib.diffkv_attn_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int]
     lib.diffkv_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.diffkv_attn_validate.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int]
@@ -150,3 +153,26 @@ def diffkv_attn_verify(*args, **kwargs):
 
 def diffkv_attn_prefill(*args, **kwargs):
     _call("diffkv_attn_prefill", *args, **kwargs)
+
+
+def prepared_kv_write(desc, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_lens,
+                      k_scale=1.0, v_scale=1.0, stream=None):
+    """Like prepared_call, for diffkv_kv_write."""
+    fn = load_library().diffkv_kv_write
+    args = (ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_table), _ptr(seq_lens), _ptr(q_lens), float(k_scale), float(v_scale),
+            _stream(stream))
+    keep = (desc, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_lens)
+
+    def call():
+        status = fn(*args)
+        if status != OK:
+            raise DiffKVError(f"diffkv_kv_write: {diffkv_attn_strerror(status)} (status {status})")
+    call.keep_alive = keep
+    return call
+
+
+def diffkv_kv_write(desc, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_lens,
+                    k_scale=1.0, v_scale=1.0, stream=None):
+    prepared_kv_write(desc, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_lens,
+                      k_scale, v_scale, stream)()

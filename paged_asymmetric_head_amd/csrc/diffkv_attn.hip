@@ -13,6 +13,7 @@
 #include "plan.hpp"
 #include "split_attn.hpp"
 #include "prefill_attn.hpp"
+#include "kv_write.hpp"
 
 using namespace diffkv;
 
@@ -241,6 +242,41 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
   return e == hipSuccess ? DIFFKV_OK : DIFFKV_HIP_ERROR;
 }
 
+int run_kv_write(const diffkv_attn_desc* d, const void* k_new, const void* v_new, void* k_cache,
+                 void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                 const int32_t* q_lens, float k_scale, float v_scale, hipStream_t stream) {
+  const int st = validate_desc(d, DIFFKV_ENTRY_PREFILL);
+  if (st != DIFFKV_OK) return st;
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !seq_lens)
+    return DIFFKV_INVALID_ARGUMENT;
+  if (!q_lens && d->max_q_len != 1) return DIFFKV_INVALID_ARGUMENT;
+  const bool fp8 = d->kv_dtype == DIFFKV_KV_FP8_E4M3;
+  if (fp8 && !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return DIFFKV_INVALID_ARGUMENT;
+  KvWriteArgs a{};
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.k_cache = static_cast<uint8_t*>(k_cache);
+  a.v_cache = static_cast<uint8_t*>(v_cache);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.q_lens = q_lens;
+  a.hkv = d->num_kv_heads;
+  a.log2_page = ilog2(d->page_size);
+  a.bt_stride = d->block_table_stride;
+  a.num_pages = d->num_pages;
+  a.total_q = d->total_q;
+  a.k_scale = fp8 ? k_scale : 1.f;
+  a.v_scale = fp8 ? v_scale : 1.f;
+  void* args[] = {&a};
+  const long long units = (long long)d->max_q_len * d->num_kv_heads * (kKUnits + kVUnits);
+  const dim3 grid((unsigned)((units + 255) / 256), d->batch);
+  const void* fn = fp8 ? reinterpret_cast<const void*>(&kv_write_kernel<true>)
+                       : reinterpret_cast<const void*>(&kv_write_kernel<false>);
+  return launch_main(fn, grid, dim3(256), args, stream) == hipSuccess ? DIFFKV_OK
+                                                                       : DIFFKV_HIP_ERROR;
+}
+
 }  // namespace
 
 extern "C" {
@@ -276,6 +312,14 @@ int diffkv_attn_prefill(const diffkv_attn_desc* desc, const void* q, const void*
   return run_entry(DIFFKV_ENTRY_PREFILL, desc, q, k_cache, v_cache, block_table, seq_lens, q_lens,
                    window, sinks, k_scale, v_scale, softmax_scale, out, lse_out, count_out,
                    workspace, workspace_bytes, stream);
+}
+
+int diffkv_kv_write(const diffkv_attn_desc* desc, const void* k_new, const void* v_new,
+                    void* k_cache, void* v_cache, const int32_t* block_table,
+                    const int32_t* seq_lens, const int32_t* q_lens, float k_scale, float v_scale,
+                    hipStream_t stream) {
+  return run_kv_write(desc, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_lens,
+                      k_scale, v_scale, stream);
 }
 
 size_t diffkv_attn_workspace_bytes(const diffkv_attn_desc* desc, int entry) {

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "diffkv_attn.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(diffkv_attn_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(diffkv_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("diffkv_attn_decode", "diffkv_attn_verify", "diffkv_attn_prefill",
               "diffkv_attn_workspace_bytes", "diffkv_attn_validate", "diffkv_attn_strerror",
-              "diffkv_attn_num_splits"):
+              "diffkv_attn_num_splits", "diffkv_kv_write"):
         assert n in names
 
 
@@ -119,3 +119,27 @@ def test_entry_rejects_before_touching_the_gpu(lib):
     st = fn(ctypes.byref(d), None, None, None, None, None, None, 0, None, 1.0, 1.0, 1.0,
             None, None, None, None, 0, None)
     assert st == B.INVALID_ARGUMENT
+
+
+def test_kv_write_rejects_before_touching_the_gpu(lib):
+    """Descriptor, pointer and scale errors of the KV write return synchronously."""
+    fn = lib.diffkv_kv_write
+    fake = 256                      # never dereferenced: every case fails its checks first
+    ptrs = [fake] * 7
+
+    def call(d, ptrs=ptrs, ks=1.0, vs=1.0):
+        return fn(ctypes.byref(d), *ptrs, ks, vs, None)
+
+    assert call(good_desc(head_dim_v=64)) == B.UNSUPPORTED
+    assert call(good_desc(page_size=96)) == B.UNSUPPORTED
+    assert call(good_desc(total_q=0)) == B.INVALID_ARGUMENT
+    for i in range(6):              # k_new, v_new, caches, block table, seq_lens
+        p = list(ptrs)
+        p[i] = None
+        assert call(good_desc(), p) == B.INVALID_ARGUMENT, i
+    p = list(ptrs)
+    p[6] = None                     # q_lens NULL needs max_q_len == 1
+    assert call(good_desc(), p) == B.INVALID_ARGUMENT
+    fp8 = good_desc(kv_dtype=B.KV_FP8_E4M3)
+    for ks, vs in ((0.0, 1.0), (1.0, -2.0), (float("nan"), 1.0), (1.0, float("inf"))):
+        assert call(fp8, ks=ks, vs=vs) == B.INVALID_ARGUMENT, (ks, vs)
