@@ -43,9 +43,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ENTRY_OF = {"tiny_decode": "decode", "batched_decode": "decode", "verify_long": "verify",
             "swa_sinks_fp8_p1": "verify", "swa_sinks_fp8_p128": "verify",
-            "chunked_prefill": "prefill"}
+            "chunked_prefill": "prefill", "mixed_batch": "mixed"}
 KERNEL_OF_ENTRY = {"decode": "split_attn_kernel", "verify": "split_attn_kernel",
-                   "prefill": "prefill_attn_kernel"}
+                   "prefill": "prefill_attn_kernel",
+                   "mixed": "split_attn_kernel + prefill_attn_kernel"}
 
 
 def parse_args():
@@ -94,9 +95,10 @@ class HipEvents:
         return float(ms.value)
 
 
-def algorithmic_work(inp):
+def algorithmic_work(inp, q_lo=1, q_hi=None):
     """Bytes of the KV rows the visible keys occupy (each read once per
-    (sequence, KV head)), (query row, visible key) pairs and their flops."""
+    (sequence, KV head)), (query row, visible key) pairs and their flops,
+    over the sequences with q_lo <= q_len <= q_hi."""
     import numpy as np
     esize = 1 if inp.kv_dtype == "fp8" else 2
     keys = 0
@@ -104,6 +106,8 @@ def algorithmic_work(inp):
     qctx = 0
     for b in range(inp.batch):
         L, n = int(inp.seq_lens[b]), int(inp.q_lens[b])
+        if n < q_lo or (q_hi is not None and n > q_hi):
+            continue
         p = L - n + np.arange(n)
         lo = np.maximum(0, p - inp.window + 1) if inp.window > 0 else np.zeros_like(p)
         keys += int(p.max() + 1 - lo.min())
@@ -324,10 +328,25 @@ def write_traffic(workload, fetch_csv, write_csv):
     print(json.dumps({workload: rec}))
 
 
+MIXED_SPLIT_MAX_Q = 16     # mixed calls: q_len <= 16 on the split kernels, longer on prefill
+
+
 def roofline(m, sha, name):
     w = m["work"]
     ms = m["kernel_ms_mean"]
     traffic = measured_traffic(name, sha)
+    if m["entry"] == "mixed":
+        # Two kernels in sequence: the time each part needs at its own bound
+        # (KV bytes of the short sequences at HBM peak, flops of the long ones
+        # at bf16 MFMA peak), summed, against the measured step.
+        ws = algorithmic_work(m["inp"], q_hi=MIXED_SPLIT_MAX_Q)
+        wp = algorithmic_work(m["inp"], q_lo=MIXED_SPLIT_MAX_Q + 1)
+        bound_ms = 1e3 * (ws["kv_bytes"] / (HBM_PEAK_GBS * 1e9) + wp["flops"] / (BF16_PEAK_TFLOPS * 1e12))
+        return {"bound": "hbm+mfma", "bound_ms": round(bound_ms, 5), "step_ms": round(m["ms_per_step"], 5),
+                "frac": round(bound_ms / m["ms_per_step"], 4), "traffic": None,
+                "kernel": KERNEL_OF_ENTRY["mixed"], "split_part_kv_bytes": ws["kv_bytes"],
+                "prefill_part_flops": wp["flops"],
+                "split_kernel_ms": round(ms, 5)}
     if m["entry"] == "prefill":
         achieved = w["flops"] / (ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
@@ -446,7 +465,8 @@ def main():
     del m
     if not args.no_extra:
         extra = {}
-        for other in ("verify_long", "swa_sinks_fp8_p1", "swa_sinks_fp8_p128", "chunked_prefill"):
+        for other in ("verify_long", "swa_sinks_fp8_p1", "swa_sinks_fp8_p128", "chunked_prefill",
+                      "mixed_batch"):
             if other == name:
                 continue
             print(f"[bench] {other}: generating and measuring", file=sys.stderr, flush=True)

@@ -26,7 +26,7 @@
  * used as stored), m the running maximum, and the sink term present only
  * when sinks != NULL.  s_h is a logit in the already-scaled domain.
  *
- * All three entry points compute this same function; they differ only in
+ * All four entry points compute this same function; they differ only in
  * how the work is cut up and in the q_len they accept.
  */
 #ifndef DIFFKV_ATTN_H
@@ -50,7 +50,8 @@ enum {
 };
 
 /* Entry selectors for diffkv_attn_workspace_bytes / diffkv_attn_validate. */
-enum { DIFFKV_ENTRY_DECODE = 0, DIFFKV_ENTRY_VERIFY = 1, DIFFKV_ENTRY_PREFILL = 2 };
+enum { DIFFKV_ENTRY_DECODE = 0, DIFFKV_ENTRY_VERIFY = 1, DIFFKV_ENTRY_PREFILL = 2,
+       DIFFKV_ENTRY_MIXED = 3 };
 
 /* K/V storage formats. */
 enum {
@@ -78,7 +79,8 @@ typedef struct diffkv_attn_desc {
   int32_t total_q;             /* == sum of q_lens: rows of q and out               */
   int32_t kv_dtype;            /* DIFFKV_KV_BF16 or DIFFKV_KV_FP8_E4M3              */
   int32_t force_num_splits;    /* 0 = automatic; > 0 forces the key-axis split count
-                                  (decode/verify only; a test hook)                 */
+                                  (decode, verify and mixed's split-KV part; a test
+                                  hook)                                             */
 } diffkv_attn_desc;
 
 /*
@@ -129,6 +131,16 @@ typedef struct diffkv_attn_desc {
  *                      GPU, as the split-KV fix for the verify step does).
  * diffkv_attn_prefill: any q_len (chunked causal prefill over a paged prefix,
  *                      large query tiles on the matrix cores).
+ * diffkv_attn_mixed:   any q_len per sequence, for batches that mix decode,
+ *                      verify and prefill sequences ("sammysun0711/sglang PR
+ *                      35", file table: ordinary decode prepared alongside
+ *                      speculative verify; "diffbot/MiMo-V2.6-Flash-RL-FP8KV-
+ *                      W4A8-2x-RTX-PRO-6000", Credits: mixed-batch changes):
+ *                      the sequences with q_len <= 16 take the split-KV kernels,
+ *                      the others the prefill kernel, both enqueued on
+ *                      `stream` in that order.  Which path a sequence takes
+ *                      is decided on the device from q_lens, so the launch
+ *                      shapes still depend on the descriptor alone.
  */
 int diffkv_attn_decode(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
                        const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
@@ -150,6 +162,13 @@ int diffkv_attn_prefill(const diffkv_attn_desc* desc, const void* q, const void*
                         float v_scale, float softmax_scale, void* out, float* lse_out,
                         int32_t* count_out, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+int diffkv_attn_mixed(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* q_lens, int32_t window, const float* sinks, float k_scale,
+                      float v_scale, float softmax_scale, void* out, float* lse_out,
+                      int32_t* count_out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
 
 /*
  * Paged KV write: stores the new tokens' K and V rows into their cache slots,
@@ -194,12 +213,14 @@ size_t diffkv_attn_workspace_bytes(const diffkv_attn_desc* desc, int entry);
 int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry);
 
 /* Number of key-axis splits the entry launches for this descriptor and
- * window (1 for prefill; 0 for an invalid descriptor).  Host only. */
+ * window (1 for prefill; for mixed, the split count of its split-KV part;
+ * 0 for an invalid descriptor).  Host only. */
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window);
 
 /* Profiling hook.  Arms two caller-created HIP events for the next
- * decode/verify/prefill/kv_write call made on this host thread: that call's
- * main kernel (not the split merge) is dispatched with them as its
+ * decode/verify/prefill/mixed/kv_write call made on this host thread: that
+ * call's first main kernel (not the split merge; for mixed, the split-KV
+ * kernel) is dispatched with them as its
  * start and stop events (hipExtLaunchKernel), so hipEventElapsedTime(start,
  * stop) is that kernel's execution time.  The hook disarms after one call;
  * passing two NULLs disarms it.  Returns DIFFKV_INVALID_ARGUMENT if exactly

@@ -13,9 +13,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = range(5)
-ENTRY_DECODE, ENTRY_VERIFY, ENTRY_PREFILL = 0, 1, 2
+ENTRY_DECODE, ENTRY_VERIFY, ENTRY_PREFILL, ENTRY_MIXED = 0, 1, 2, 3
 KV_BF16, KV_FP8_E4M3 = 0, 1
-ENTRIES = {"decode": ENTRY_DECODE, "verify": ENTRY_VERIFY, "prefill": ENTRY_PREFILL}
+ENTRIES = {"decode": ENTRY_DECODE, "verify": ENTRY_VERIFY, "prefill": ENTRY_PREFILL,
+           "mixed": ENTRY_MIXED}
 
 
 class DiffKVError(RuntimeError):
@@ -48,7 +49,8 @@ def load_library():
     if not os.path.exists(path):
         raise DiffKVError(f"{path} is not built; run __graft_entry__.build() first")
     lib = ctypes.CDLL(path)
-    for name in ("diffkv_attn_decode", "diffkv_attn_verify", "diffkv_attn_prefill"):
+    for name in ("diffkv_attn_decode", "diffkv_attn_verify", "diffkv_attn_prefill",
+                 "diffkv_attn_mixed"):
         fn = getattr(lib, name)
         fn.argtypes = _ENTRY_ARGS
         fn.restype = ctypes.c_int
@@ -153,6 +155,10 @@ def diffkv_attn_verify(*args, **kwargs):
 
 def diffkv_attn_prefill(*args, **kwargs):
     _call("diffkv_attn_prefill", *args, **kwargs)
+
+
+def diffkv_attn_mixed(*args, **kwargs):
+    _call("diffkv_attn_mixed", *args, **kwargs)
 
 
 def prepared_kv_write(desc, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_lens,

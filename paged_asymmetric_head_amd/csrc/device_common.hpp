@@ -11,6 +11,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -75,6 +76,15 @@ __device__ __forceinline__ f32x2 unpack_bf16x2(uint32_t w) {
   return f32x2{__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xFFFF0000u)};
 }
 
+// Two fp32 -> two fp16 in one word (round to nearest even), and back.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+__device__ __forceinline__ f32x2 unpack_f16x2(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+}
+
 // Four OCP E4M3FN codes (one 32-bit word, byte 0 first) -> four bf16 codes in
 // two words, with gfx950's packed converter at scale 1.0.  Every finite
 // E4M3 value has at most 4 significant bits and an exponent in [-9, 8], so
@@ -118,6 +128,9 @@ __device__ __forceinline__ int wave_sum_int(int v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+
+// Value of x in lane `lane` (wave-uniform) for every lane.
+__device__ __forceinline__ int read_lane(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
 
 // Packed query row where sequence b starts: sum of q_lens[0..b).  One wave
 // computes it cooperatively (a strided sum and a wave reduction).

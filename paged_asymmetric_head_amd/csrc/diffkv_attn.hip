@@ -33,7 +33,7 @@ int ilog2(int x) {
 
 int validate_desc(const diffkv_attn_desc* d, int entry) {
   if (d == nullptr) return DIFFKV_INVALID_ARGUMENT;
-  if (entry < DIFFKV_ENTRY_DECODE || entry > DIFFKV_ENTRY_PREFILL) return DIFFKV_INVALID_ARGUMENT;
+  if (entry < DIFFKV_ENTRY_DECODE || entry > DIFFKV_ENTRY_MIXED) return DIFFKV_INVALID_ARGUMENT;
   if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1) return DIFFKV_INVALID_ARGUMENT;
   if (d->num_q_heads % d->num_kv_heads != 0) return DIFFKV_INVALID_ARGUMENT;
   if (d->head_dim_qk != kHeadDimQK || d->head_dim_v != kHeadDimV) return DIFFKV_UNSUPPORTED;
@@ -51,8 +51,8 @@ int validate_desc(const diffkv_attn_desc* d, int entry) {
   // Launch-shape limits.
   if ((long long)d->batch * d->num_kv_heads > kMaxGridYZ) return DIFFKV_UNSUPPORTED;
   if (entry != DIFFKV_ENTRY_PREFILL) {
-    const SplitPlan p = plan_split(*d, 0, true);
-    if (p.n_qtiles > kMaxGridYZ) return DIFFKV_UNSUPPORTED;
+    const SplitPlan p = plan_split(split_part_desc(*d, entry), 0);
+    if (p.grid_x > INT32_MAX) return DIFFKV_UNSUPPORTED;
   }
   if ((long long)d->total_q * d->num_q_heads > (1LL << 31) / kHeadDimQK) return DIFFKV_UNSUPPORTED;
   return DIFFKV_OK;
@@ -104,22 +104,23 @@ hipError_t dispatch_split(const SplitArgs& a, int rt, bool upage, dim3 grid, boo
   }
 }
 
-// Merge shape by split count: one wave when its loads cover every split
-// (16 or 32), else four waves covering 128 splits per pass.
+// Merge shape by the bound on chunks per pair: one wave with 16 loads when
+// that covers every chunk, else four waves with 32 loads each (128 chunks per
+// pass), of which a pair of at most 32 chunks uses one.
 template <int ROWS>
 const void* merge_kernel_for(int splits, int& threads) {
   if (splits <= 16) { threads = 64; return reinterpret_cast<const void*>(&split_merge_kernel<ROWS, 1, 16>); }
-  if (splits <= 32) { threads = 64; return reinterpret_cast<const void*>(&split_merge_kernel<ROWS, 1, 32>); }
   threads = 256;
   return reinterpret_cast<const void*>(&split_merge_kernel<ROWS, 4, 32>);
 }
 
-hipError_t launch_merge(const SplitArgs& a, int rows, dim3 grid, hipStream_t stream) {
+hipError_t launch_merge(const SplitArgs& a, int rows, int max_chunks, dim3 grid,
+                        hipStream_t stream) {
   void* args[] = {const_cast<SplitArgs*>(&a)};
   int threads = 0;
-  const void* fn = rows == 16 ? merge_kernel_for<16>(a.num_splits, threads)
-                 : rows == 32 ? merge_kernel_for<32>(a.num_splits, threads)
-                              : merge_kernel_for<64>(a.num_splits, threads);
+  const void* fn = rows == 16 ? merge_kernel_for<16>(max_chunks, threads)
+                 : rows == 32 ? merge_kernel_for<32>(max_chunks, threads)
+                              : merge_kernel_for<64>(max_chunks, threads);
   return hipLaunchKernel(fn, grid, dim3(threads), args, 0, stream);
 }
 
@@ -170,40 +171,7 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
   }
 
   const bool upage = d->page_size >= kTileKeys;
-  if (entry == DIFFKV_ENTRY_PREFILL) {
-    // One workgroup per 128 query rows of a (sequence, KV head); the many
-    // rows of a chunk fill the GPU without splitting the keys.
-    SplitArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.k_cache = static_cast<const uint8_t*>(k_cache);
-    a.v_cache = static_cast<const uint8_t*>(v_cache);
-    a.block_table = block_table;
-    a.seq_lens = seq_lens;
-    a.q_lens = q_lens;
-    a.sinks = sinks;
-    a.out = static_cast<uint16_t*>(out);
-    a.lse_out = lse_out;
-    a.count_out = count_out;
-    a.hq = d->num_q_heads;
-    a.hkv = d->num_kv_heads;
-    a.group = G;
-    a.log2_page = ilog2(d->page_size);
-    a.bt_stride = d->block_table_stride;
-    a.window = window;
-    a.n_qtiles = prefill_row_blocks(*d);
-    a.num_splits = 1;
-    a.scale_log2 = softmax_scale * ks * kLog2e;
-    a.v_scale = vs;
-    const dim3 grid(a.n_qtiles, d->batch * d->num_kv_heads);
-    const hipError_t e = fp8 ? dispatch_prefill<true>(a, upage, count_out != nullptr, grid, stream)
-                             : dispatch_prefill<false>(a, upage, count_out != nullptr, grid, stream);
-    return e == hipSuccess ? DIFFKV_OK : DIFFKV_HIP_ERROR;
-  }
-
-  const SplitPlan plan = plan_split(*d, window, true, kSplitWavesPerEu);
-  if (plan.num_splits > 1 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
-    return DIFFKV_WORKSPACE_TOO_SMALL;
-
+  const bool count = count_out != nullptr;
   SplitArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k_cache = static_cast<const uint8_t*>(k_cache);
@@ -215,31 +183,61 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
   a.out = static_cast<uint16_t*>(out);
   a.lse_out = lse_out;
   a.count_out = count_out;
-  if (plan.num_splits > 1) {
-    a.part_o = static_cast<uint16_t*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          ((plan.part_o_bytes + 255) / 256) * 256);
-  }
+  a.batch = d->batch;
   a.hq = d->num_q_heads;
   a.hkv = d->num_kv_heads;
   a.group = G;
   a.log2_page = ilog2(d->page_size);
   a.bt_stride = d->block_table_stride;
   a.window = window;
-  a.n_qtiles = plan.n_qtiles;
-  a.num_splits = plan.num_splits;
+  a.q_lo = 1;
+  a.q_hi = INT32_MAX;
   a.scale_log2 = softmax_scale * ks * kLog2e;
   a.v_scale = vs;
 
-  const dim3 grid(plan.num_splits, plan.n_qtiles, d->batch * d->num_kv_heads);
-  const bool direct = plan.num_splits == 1;
-  hipError_t e =
-      fp8 ? dispatch_split<true>(a, plan.row_tiles, upage, grid, direct, count_out != nullptr, stream)
-          : dispatch_split<false>(a, plan.row_tiles, upage, grid, direct, count_out != nullptr, stream);
-  if (e == hipSuccess && !direct)
-    e = launch_merge(a, plan.rows,
-                     dim3(d->max_q_len * G, d->batch * d->num_kv_heads), stream);
-  return e == hipSuccess ? DIFFKV_OK : DIFFKV_HIP_ERROR;
+  // Split-KV part: decode and verify, and a mixed call's short sequences.
+  if (entry != DIFFKV_ENTRY_PREFILL) {
+    const diffkv_attn_desc sd = split_part_desc(*d, entry);
+    const SplitPlan plan = plan_split(sd, window, kSplitWavesPerEu);
+    if (!plan.direct && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+      return DIFFKV_WORKSPACE_TOO_SMALL;
+    SplitArgs sa = a;
+    if (!plan.direct) {
+      char* ws = static_cast<char*>(workspace);
+      sa.part_o = reinterpret_cast<uint16_t*>(ws);
+      sa.part_lse = reinterpret_cast<f32x2*>(ws + align256(plan.part_o_bytes));
+      sa.pair_chunks = reinterpret_cast<i32x2*>(ws + align256(plan.part_o_bytes) +
+                                                align256(plan.part_lse_bytes));
+    }
+    sa.n_qtiles = plan.n_qtiles;
+    sa.slots = plan.slots;
+    sa.force_splits = d->force_num_splits;
+    sa.chunk_bound = (int)plan.grid_x;
+    if (entry == DIFFKV_ENTRY_MIXED) sa.q_hi = kMixedSplitMaxQ;
+    const dim3 grid((unsigned)plan.grid_x, d->num_kv_heads);
+    hipError_t e =
+        fp8 ? dispatch_split<true>(sa, plan.row_tiles, upage, grid, plan.direct, count, stream)
+            : dispatch_split<false>(sa, plan.row_tiles, upage, grid, plan.direct, count, stream);
+    if (e == hipSuccess && !plan.direct)
+      e = launch_merge(sa, plan.rows, plan.max_chunks,
+                       dim3(sd.max_q_len * G, d->batch * d->num_kv_heads), stream);
+    if (e != hipSuccess) return DIFFKV_HIP_ERROR;
+  }
+
+  // Prefill part: one workgroup per 256 query rows of a (sequence, KV head);
+  // the many rows of a chunk fill the GPU without splitting the keys.
+  const bool prefill_part = entry == DIFFKV_ENTRY_PREFILL ||
+                            (entry == DIFFKV_ENTRY_MIXED && d->max_q_len > kMixedSplitMaxQ);
+  if (prefill_part) {
+    SplitArgs pa = a;
+    pa.n_qtiles = prefill_row_blocks(*d);
+    if (entry == DIFFKV_ENTRY_MIXED) pa.q_lo = kMixedSplitMaxQ + 1;
+    const dim3 grid(pa.n_qtiles, d->batch * d->num_kv_heads);
+    const hipError_t e = fp8 ? dispatch_prefill<true>(pa, upage, count, grid, stream)
+                             : dispatch_prefill<false>(pa, upage, count, grid, stream);
+    if (e != hipSuccess) return DIFFKV_HIP_ERROR;
+  }
+  return DIFFKV_OK;
 }
 
 int run_kv_write(const diffkv_attn_desc* d, const void* k_new, const void* v_new, void* k_cache,
@@ -322,10 +320,21 @@ int diffkv_kv_write(const diffkv_attn_desc* desc, const void* k_new, const void*
                       k_scale, v_scale, stream);
 }
 
+int diffkv_attn_mixed(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* q_lens, int32_t window, const float* sinks, float k_scale,
+                      float v_scale, float softmax_scale, void* out, float* lse_out,
+                      int32_t* count_out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return run_entry(DIFFKV_ENTRY_MIXED, desc, q, k_cache, v_cache, block_table, seq_lens, q_lens,
+                   window, sinks, k_scale, v_scale, softmax_scale, out, lse_out, count_out,
+                   workspace, workspace_bytes, stream);
+}
+
 size_t diffkv_attn_workspace_bytes(const diffkv_attn_desc* desc, int entry) {
   if (validate_desc(desc, entry) != DIFFKV_OK) return 0;
   if (entry == DIFFKV_ENTRY_PREFILL) return 0;
-  return plan_split(*desc, 0, true).workspace_bytes;
+  return plan_split(split_part_desc(*desc, entry), 0).workspace_bytes;
 }
 
 int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry) {
@@ -335,8 +344,7 @@ int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry) {
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window) {
   if (validate_desc(desc, entry) != DIFFKV_OK) return 0;
   if (entry == DIFFKV_ENTRY_PREFILL) return 1;
-  return plan_split(*desc, window, true, kSplitWavesPerEu)
-      .num_splits;
+  return plan_split(split_part_desc(*desc, entry), window, kSplitWavesPerEu).max_chunks;
 }
 
 int diffkv_attn_profile_next_call(hipEvent_t start, hipEvent_t stop) {

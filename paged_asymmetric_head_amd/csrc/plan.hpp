@@ -29,10 +29,15 @@ inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 struct SplitPlan {
   int row_tiles = 1;      // 16-row MFMA tiles per workgroup
   int rows = 16;          // query rows per workgroup (16 * row_tiles)
-  int n_qtiles = 1;       // workgroups along the query rows of one (sequence, KV head)
-  int num_splits = 1;     // workgroups along the key axis
-  size_t part_o_bytes = 0, part_lse_bytes = 0, workspace_bytes = 0;
+  int n_qtiles = 1;       // query tiles per (sequence, KV head)
+  bool direct = true;     // one chunk per pair: no partials, no merge
+  int slots = 1;          // balanced plan: target chunks per KV head
+  int max_chunks = 1;     // bound on the chunks of one pair (picks the merge shape)
+  long long grid_x = 1;   // workgroups per KV head
+  size_t part_o_bytes = 0, part_lse_bytes = 0, pair_bytes = 0, workspace_bytes = 0;
 };
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Upper bound on the keys one (sequence, KV head, query tile) reads.
 inline long long max_keys_bound(const diffkv_attn_desc& d, int window) {
@@ -64,51 +69,64 @@ inline long long max_keys_bound(const diffkv_attn_desc& d, int window) {
 template <bool FP8> constexpr int kSplitStages = FP8 ? DIFFKV_FP8_STAGES : DIFFKV_BF16_STAGES;
 constexpr int kSplitWavesPerEu = DIFFKV_SPLIT_WAVES_PER_EU;
 
-// Split count: one resident round of workgroups over the 256 CUs (a second
+// Split plan from host bounds.  The kernels cut the keys on the device
+// (balanced chunks of C = max(kMinTilesPerSplit, ceil(T / slots)) tiles, T
+// the key tiles of the whole call), so the host fixes only the bounds: slots
+// = one resident round of workgroups over the 256 CUs per KV head (a second
 // round would pay the start-up chain seq_lens -> block table -> data again),
-// but never fewer than `kMinTilesPerSplit` tiles per split (the split
-// partials are extra traffic, so short splits do not pay).  Monotone in the
-// key bound, so the workspace sized for full attention covers every window;
-// the workspace is sized for the largest target (4 workgroups per CU).
+// at most slots + pairs chunks per KV head (each pair's last chunk may be
+// short), and no split at all when no pair can hold more than
+// kMinTilesPerSplit tiles (short windows).  A larger wgs_per_cu only grows
+// the bounds, so the workspace sized for 4 workgroups per CU covers every
+// launch.
 constexpr int kMinTilesPerSplit = 4;
 
-inline SplitPlan plan_split(const diffkv_attn_desc& d, int window, bool allow_split,
-                            int wgs_per_cu = 4) {
+inline SplitPlan plan_split(const diffkv_attn_desc& d, int window, int wgs_per_cu = 4) {
   SplitPlan p;
   const int G = d.num_q_heads / d.num_kv_heads;
   const long long rows_pair = (long long)d.max_q_len * G;
   p.row_tiles = split_row_tiles((int)(rows_pair < 64 ? rows_pair : 64));
   p.rows = 16 * p.row_tiles;
   p.n_qtiles = ceil_div(rows_pair, p.rows);
-  const long long pairs = (long long)d.batch * d.num_kv_heads * p.n_qtiles;
-  const long long tiles = ceil_div(max_keys_bound(d, window), kTileKeys) + 1;
-  int s = 1;
-  if (allow_split) {
-    if (d.force_num_splits > 0) {
-      s = d.force_num_splits;
-    } else {
-      const long long target = (long long)kTargetCUs * wgs_per_cu;
-      long long want = (target + pairs - 1) / pairs;
-      long long cap = tiles / kMinTilesPerSplit;
-      if (cap < 1) cap = 1;
-      if (want > cap) want = cap;
-      if (want < 1) want = 1;
-      s = (int)want;
-    }
+  const long long pairs = (long long)d.batch * p.n_qtiles;
+  const long long max_tiles = ceil_div(max_keys_bound(d, window), kTileKeys) + 1;
+  const int per_head = kTargetCUs * wgs_per_cu / d.num_kv_heads;
+  p.slots = per_head > 1 ? per_head : 1;
+  if (d.force_num_splits > 0) {
+    p.direct = d.force_num_splits == 1;
+    p.max_chunks = d.force_num_splits;
+    p.grid_x = pairs * d.force_num_splits;
+  } else {
+    p.direct = max_tiles <= kMinTilesPerSplit;
+    const long long kmax = ceil_div(max_tiles, kMinTilesPerSplit);
+    p.max_chunks = p.direct ? 1 : (int)(kmax < p.slots ? kmax : p.slots);
+    p.grid_x = p.direct ? pairs : p.slots + pairs;
   }
-  p.num_splits = s;
-  if (s > 1) {
-    const size_t prow = (size_t)pairs * s * p.rows;
-    p.part_o_bytes = prow * kHeadDimV * sizeof(uint16_t);   // bf16 partial rows
-    p.part_lse_bytes = prow * sizeof(float);
-    p.workspace_bytes = ((p.part_o_bytes + 255) / 256) * 256 + ((p.part_lse_bytes + 255) / 256) * 256;
+  if (!p.direct) {
+    const size_t prow = (size_t)p.grid_x * d.num_kv_heads * p.rows;
+    p.part_o_bytes = prow * kHeadDimV * sizeof(uint16_t);   // fp16 partial rows
+    p.part_lse_bytes = prow * 2 * sizeof(float);             // lse and row exponent
+    p.pair_bytes = (size_t)pairs * 2 * sizeof(int32_t);      // first chunk id, chunk count
+    p.workspace_bytes = align256(p.part_o_bytes) + align256(p.part_lse_bytes) + align256(p.pair_bytes);
   }
   return p;
 }
 
 // Prefill: workgroups of kPrefillRows query rows along one (sequence, KV
-// head), one 16-row tile per wave.
+// head), two 16-row tiles per wave.
 constexpr int kPrefillRows = 256;
+
+// Mixed batches: sequences with at most this many new tokens (the verify
+// limit) go to the split kernel, longer ones to the prefill kernel.
+constexpr int kMixedSplitMaxQ = 16;
+
+// The descriptor the split part of a call is planned from: a mixed call's
+// split kernel sees only sequences of at most kMixedSplitMaxQ new tokens.
+inline diffkv_attn_desc split_part_desc(const diffkv_attn_desc& d, int entry) {
+  diffkv_attn_desc s = d;
+  if (entry == DIFFKV_ENTRY_MIXED && s.max_q_len > kMixedSplitMaxQ) s.max_q_len = kMixedSplitMaxQ;
+  return s;
+}
 inline int prefill_row_blocks(const diffkv_attn_desc& d) {
   return ceil_div((long long)d.max_q_len * (d.num_q_heads / d.num_kv_heads), kPrefillRows);
 }

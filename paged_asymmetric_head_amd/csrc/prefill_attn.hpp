@@ -67,7 +67,7 @@ void prefill_attn_kernel(const SplitArgs a) {
 
   const int L = a.seq_lens[b];
   const int n = a.q_lens ? a.q_lens[b] : 1;
-  if (qb * kPrefillRows >= n * G) return;
+  if (qb * kPrefillRows >= n * G || n < a.q_lo || n > a.q_hi) return;
   int kv_lo, kv_hi;
   qtile_key_range(L, n, G, qb, kPrefillRows, a.window, kv_lo, kv_hi);
   const int t_begin = kv_lo / kTileKeys;

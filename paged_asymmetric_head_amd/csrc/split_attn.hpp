@@ -39,28 +39,146 @@ struct SplitArgs {
   const int32_t* seq_lens;
   const int32_t* q_lens;
   const float* sinks;
-  uint16_t* part_o;     // bf16 normalised partial rows [.., 128]
-  float* part_lse;      // base-2 log-sum-exp of each partial row
+  uint16_t* part_o;     // fp16 partial rows [.., 128]: normalised row * 2^-e
+  f32x2* part_lse;      // per partial row: base-2 log-sum-exp, exponent e
+  i32x2* pair_chunks;   // per (sequence, query tile): first chunk id, chunk count
   uint16_t* out;
   float* lse_out;
   int32_t* count_out;
-  int hq, hkv, group, log2_page, bt_stride, window;
-  int n_qtiles, num_splits;
+  int batch, hq, hkv, group, log2_page, bt_stride, window;
+  int n_qtiles;       // query tiles per (sequence, KV head) the launch covers
+  int slots;          // balanced plan: target chunks per KV head (one resident round)
+  int force_splits;   // > 0: every (sequence, query tile) takes exactly this many chunks
+  int chunk_bound;    // chunk ids stay below this (the workspace holds that many)
+  int q_lo, q_hi;     // this launch takes the sequences with q_lo <= q_len <= q_hi
   float scale_log2;   // softmax_scale * k_scale * log2(e)
   float v_scale;      // v_scale for FP8 caches, 1 for bf16
 };
 
-// Tiles of split s among S equal shares of the aligned tile range.
+// Tiles of chunk s among S equal shares of the aligned tile range.
 __device__ __forceinline__ void split_tiles(int kv_lo, int kv_hi, int S, int s, int& t_begin,
-                                            int& t_end, int& n_valid) {
+                                            int& t_end) {
   const int t0 = kv_lo / kTileKeys;
   const int t1 = (kv_hi + kTileKeys - 1) / kTileKeys;
-  const int nt = t1 - t0;
-  const int tps = (nt + S - 1) / S;
+  const int tps = (t1 - t0 + S - 1) / S;
   t_begin = t0 + s * tps;
   t_end = min(t1, t_begin + tps);
-  n_valid = (nt + tps - 1) / tps;
 }
+
+// Balanced split plan.  The keys a (sequence, query tile) pair sees span
+// nt 64-key tiles; over the pairs of the launch (sequences with q_lo <=
+// q_len <= q_hi) they total T.  With C = max(kMinTilesPerSplit, ceil(T /
+// slots)) a pair is cut into k = ceil(nt / C) chunks of equal tile counts
+// (force_splits fixes k instead), and chunk ids number the chunks pair by
+// pair in (sequence, query tile) order.  Every split workgroup derives the
+// same plan from seq_lens and q_lens (the first chunk of each pair records
+// its chunk range for the merge), so which workgroup sums which keys
+// depends on the lengths alone (results repeat bit for bit) while the
+// launch shape depends on host bounds alone.  Long
+// and short sequences in one batch get chunks of about the same length,
+// where equal shares per sequence would leave the longest one as the tail.
+// Each wave computes the plan for itself (no LDS, no barrier).
+template <int ROWS>
+struct SplitPlanner {
+  const SplitArgs& a;
+  int C = 0;            // tiles per chunk; 0 with forced splits
+  int L0 = 0, n0 = 0;   // this lane's sequence (b = lane) of the first pass
+
+  __device__ __forceinline__ explicit SplitPlanner(const SplitArgs& args) : a(args) {}
+
+  // Lengths of sequence b0 + lane (new tokens 0 past the batch).
+  __device__ __forceinline__ void load(int b0, int& L, int& n) const {
+    const int b = b0 + lane_id();
+    L = 0;
+    n = 0;
+    if (b < a.batch) {
+      L = a.seq_lens[b];
+      n = a.q_lens ? a.q_lens[b] : 1;
+    }
+  }
+  __device__ __forceinline__ int qtiles(int n) const {
+    return n >= a.q_lo && n <= a.q_hi ? min((n * a.group + ROWS - 1) / ROWS, a.n_qtiles) : 0;
+  }
+  __device__ __forceinline__ int tiles(int L, int n, int qt) const {
+    int lo, hi;
+    qtile_key_range(L, n, a.group, qt, ROWS, a.window, lo, hi);
+    return (hi + kTileKeys - 1) / kTileKeys - lo / kTileKeys;
+  }
+  __device__ __forceinline__ int chunks(int L, int n, int qt) const {
+    return a.force_splits > 0 ? a.force_splits : (tiles(L, n, qt) + C - 1) / C;
+  }
+  // Chunks of all query tiles of a sequence (0 for one this launch skips).
+  __device__ __forceinline__ int seq_chunks(int L, int n) const {
+    int k = 0;
+    const int nq = qtiles(n);
+    for (int qt = 0; qt < nq; ++qt) k += chunks(L, n, qt);
+    return k;
+  }
+
+  __device__ __forceinline__ void init() {
+    load(0, L0, n0);
+    if (a.force_splits > 0) return;
+    int T = 0;
+    for (int b0 = 0; b0 < a.batch; b0 += 64) {
+      int L = L0, n = n0;
+      if (b0 > 0) load(b0, L, n);
+      const int nq = qtiles(n);
+      for (int qt = 0; qt < nq; ++qt) T += tiles(L, n, qt);
+    }
+    T = wave_sum_int(T);
+    C = max(kMinTilesPerSplit, (T + a.slots - 1) / a.slots);
+  }
+
+  // The pair and chunk of chunk id w, with the sequence's lengths and its
+  // first packed query row; false when w is past the last chunk.
+  __device__ __forceinline__ bool find(int w, int& b, int& qt, int& c, int& base, int& k, int& L_b,
+                                       int& n_b, int& r0) const {
+    int before = 0;                           // chunks of the earlier passes
+    int rows_before = 0;                      // new tokens of the earlier passes
+    for (int b0 = 0; b0 < a.batch; b0 += 64) {
+      int L = L0, n = n0;
+      if (b0 > 0) load(b0, L, n);
+      const int kb = seq_chunks(L, n);
+      // Inclusive prefix sums over the lanes (chunks, and new tokens for the
+      // packed row start).
+      int incl = kb, nincl = n;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        incl += lane_id() >= o ? y : 0;
+      }
+      if (a.q_lens) {
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(nincl, o, 64);
+          nincl += lane_id() >= o ? y : 0;
+        }
+      }
+      const int total = read_lane(incl, 63);
+      if (w < before + total) {
+        const int owner = __builtin_ctzll(__ballot(before + incl > w));
+        b = b0 + owner;
+        base = before + read_lane(incl - kb, owner);
+        L_b = read_lane(L, owner);
+        n_b = read_lane(n, owner);
+        r0 = a.q_lens ? rows_before + read_lane(nincl - n, owner) : b;
+        const int nq = qtiles(n_b);
+        for (qt = 0; qt < nq; ++qt) {
+          k = chunks(L_b, n_b, qt);
+          if (w < base + k) {
+            c = w - base;
+            return true;
+          }
+          base += k;
+        }
+        return false;                         // not reached
+      }
+      before += total;
+      rows_before += a.q_lens ? read_lane(nincl, 63) : 0;
+    }
+    return false;
+  }
+};
 
 template <bool FP8, int RT, bool DIRECT, bool COUNT, bool UPAGE, int NS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSplitWavesPerEu, 8)))
@@ -77,21 +195,37 @@ void split_attn_kernel(const SplitArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int rt = wave % RT, kg = wave / RT;
-  const int s = blockIdx.x, qt = blockIdx.y, bg = blockIdx.z;
-  const int b = bg / a.hkv, g = bg % a.hkv;
+  const int g = blockIdx.y;
   const int G = a.group;
 
-  const int L = a.seq_lens[b];
-  const int n = a.q_lens ? a.q_lens[b] : 1;
-  if (qt * ROWS >= n * G) return;
-  int kv_lo, kv_hi, t_begin, t_end, n_valid;
+  // Which pair and chunk: one chunk per pair when DIRECT (grid.x = pairs),
+  // else the balanced plan.
+  int b, qt, c = 0, base = 0, k = 1, L, n, r0;
+  if constexpr (DIRECT) {
+    b = blockIdx.x / a.n_qtiles;
+    qt = blockIdx.x % a.n_qtiles;
+    L = a.seq_lens[b];
+    n = a.q_lens ? a.q_lens[b] : 1;
+    r0 = -1;                                  // summed below, after the loads are out
+  } else {
+    SplitPlanner<ROWS> plan(a);
+    plan.init();
+    if (!plan.find(blockIdx.x, b, qt, c, base, k, L, n, r0) || base + c >= a.chunk_bound) return;
+    // The pair's first chunk records where the merge finds the pair.
+    if (c == 0 && tid == 0) a.pair_chunks[(size_t)b * a.n_qtiles + qt] = i32x2{base, k};
+  }
+  if (qt * ROWS >= n * G || n < a.q_lo || n > a.q_hi) return;
+  // A pair of one chunk writes its output here; the merge skips it.
+  const bool direct = DIRECT || k == 1;
+  int kv_lo, kv_hi, t_begin, t_end;
   qtile_key_range(L, n, G, qt, ROWS, a.window, kv_lo, kv_hi);
-  split_tiles(kv_lo, kv_hi, a.num_splits, s, t_begin, t_end, n_valid);
+  split_tiles(kv_lo, kv_hi, k, c, t_begin, t_end);
+  // Partial row of this chunk for row r of the tile.
+  const size_t prow0 = ((size_t)(base + c) * a.hkv + g) * ROWS;
   if (t_begin >= t_end) {
-    // An empty split still marks its rows (log-sum-exp -inf) so the merge can
-    // read every split without knowing which ones had keys.
-    if (!DIRECT && tid < ROWS && qt * ROWS + tid < n * G)
-      a.part_lse[(((size_t)bg * a.n_qtiles + qt) * a.num_splits + s) * ROWS + tid] = -INFINITY;
+    // An empty chunk (forced splits only) still marks its rows (log-sum-exp
+    // -inf) so the merge can read every chunk of the pair.
+    if (!direct && tid < ROWS && qt * ROWS + tid < n * G) a.part_lse[prow0 + tid] = f32x2{-INFINITY, 0.f};
     return;
   }
 
@@ -110,7 +244,7 @@ void split_attn_kernel(const SplitArgs a) {
     io.fetch_pages(t_begin + NS + i, pg[i]);
   }
 
-  const int r0 = seq_row_start(a.q_lens, b);
+  if constexpr (DIRECT) r0 = seq_row_start(a.q_lens, b);
 
   // The query row this lane owns in S^T / O^T.
   const int R = qt * ROWS + rt * 16 + col;
@@ -294,7 +428,7 @@ void split_attn_kernel(const SplitArgs a) {
 
   if (!row_ok) return;
   const size_t out_row = (size_t)(r0 + tok) * a.hq + h;
-  if constexpr (DIRECT) {
+  if (direct) {
     float coef;
     if (a.sinks) {
       const float s2 = a.sinks[h] * kLog2e;
@@ -313,17 +447,34 @@ void split_attn_kernel(const SplitArgs a) {
     }
     if (a.lse_out && grp == 0) a.lse_out[out_row] = (m + log2f(l)) * kLn2;
   } else {
-    const size_t prow = (((size_t)bg * a.n_qtiles + qt) * a.num_splits + s) * ROWS + rt * 16 + col;
-    // Partial rows are normalised (a convex combination of V rows), so bf16
-    // keeps fp32's range; its rounding matches the output's own.
+    const size_t prow = prow0 + rt * 16 + col;
+    // The normalised partial row (a convex combination of V rows) is stored
+    // in fp16 as a block-floating-point row: scaled by 2^-e so its largest
+    // magnitude lies in [2^14, 2^15), e kept beside the row's log-sum-exp.
+    // Each element then keeps fp16's 11 bits relative to the row maximum,
+    // so the merge adds far less than the output's own bf16 rounding (a bf16
+    // partial would round every row twice at 8 bits), and any finite V fits.
     const float inv = l > 0.f ? 1.f / l : 0.f;
+    float amax = 0.f;
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[nn][i]));
+    amax = max_over_lane_groups(amax) * inv;
+    int e = 0;
+    if (amax > 0.f) {
+      int k;
+      frexpf(amax, &k);                       // amax in [2^(k-1), 2^k)
+      e = max(k - 15, -100);                  // 2^-e stays a normal float
+    }
+    const float p2 = __builtin_amdgcn_ldexpf(1.f, -e);
     uint16_t* pp = a.part_o + prow * kHeadDimV + 4 * grp;
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn) {
-      const f32x4 v = o[nn] * inv;
-      *reinterpret_cast<u32x2*>(pp + 16 * nn) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      const f32x4 v = (o[nn] * inv) * p2;
+      *reinterpret_cast<u32x2*>(pp + 16 * nn) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
     }
-    if (grp == 0) a.part_lse[prow] = l > 0.f ? m + log2f(l) : -INFINITY;
+    if (grp == 0) a.part_lse[prow] = f32x2{l > 0.f ? m + log2f(l) : -INFINITY, (float)e};
   }
 }
 
@@ -338,8 +489,9 @@ __device__ __forceinline__ float wave_sum_all(float v) {
   return v;
 }
 
-// Combines the split partials of one query row: weights 2^(lse_s - M), the
-// sink joining the denominator, v_scale, bf16 store.  One workgroup of W
+// Combines the split partials of one query row: weights 2^(lse_s - M) (times
+// 2^e_s on the stored fp16 row), the sink joining the denominator, v_scale,
+// bf16 store.  One workgroup of W
 // waves per row.  Every split wrote its row (an empty split an lse of -inf),
 // so a pass over up to W*K splits issues all of its loads before any
 // arithmetic: every wave reads all the pass's lse values (so each has the
@@ -358,26 +510,38 @@ __global__ __launch_bounds__(64 * W) void split_merge_kernel(const SplitArgs a) 
   const int bg = blockIdx.y;
   const int b = bg / a.hkv, g = bg % a.hkv;
   const int G = a.group;
-  const int S = a.num_splits;
   const int n = a.q_lens ? a.q_lens[b] : 1;
+  if (n < a.q_lo || n > a.q_hi || R >= n * G) return;   // uniform over the workgroup
+  const i32x2 pc = a.pair_chunks[(size_t)b * a.n_qtiles + qt];
+  const int base = pc.x, S = pc.y;
+  if (S <= 1) return;                       // written by the split kernel itself
+  if (base < 0 || base + S > a.chunk_bound) return;
+  // Waves in use: one when its K loads cover every chunk of the pair.
+  const int nw = S <= K ? 1 : W;
+  if (wave >= nw) return;
   const int r0 = seq_row_start(a.q_lens, b);
 
-  const size_t prow0 = ((size_t)bg * a.n_qtiles + qt) * S * ROWS + r;
+  // Chunk j's partial row: chunk ids are consecutive within the pair.
+  const size_t prow0 = ((size_t)base * a.hkv + g) * ROWS + r;
+  const size_t pstride = (size_t)a.hkv * ROWS;
   const uint16_t* po0 = a.part_o + prow0 * kHeadDimV + 2 * lane;
   float m_run = -INFINITY, ksum = 0.f;
   f32x2 acc = f32x2{0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += PASS) {
-    float lse_l[LI];
+  for (int s0 = 0; s0 < S; s0 += nw * K) {
+    const int s1 = min(S, s0 + nw * K);     // chunks [s0, s1) in this pass
+    float lse_l[LI], e_l[LI];
 #pragma unroll
     for (int i = 0; i < LI; ++i) {
       const int j = s0 + lane + 64 * i;
-      lse_l[i] = j < S ? a.part_lse[prow0 + (size_t)j * ROWS] : -INFINITY;
+      const f32x2 le = j < s1 ? a.part_lse[prow0 + (size_t)j * pstride] : f32x2{-INFINITY, 0.f};
+      lse_l[i] = le.x;
+      e_l[i] = le.y;
     }
     uint32_t raw[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int j = min(s0 + wave + W * k, S - 1);
-      raw[k] = *reinterpret_cast<const uint32_t*>(po0 + (size_t)j * ROWS * kHeadDimV);
+      const int j = min(s0 + wave + nw * k, S - 1);
+      raw[k] = *reinterpret_cast<const uint32_t*>(po0 + (size_t)j * pstride * kHeadDimV);
     }
     float mx = lse_l[0];
 #pragma unroll
@@ -390,30 +554,30 @@ __global__ __launch_bounds__(64 * W) void split_merge_kernel(const SplitArgs a) 
     float wl[LI];
 #pragma unroll
     for (int i = 0; i < LI; ++i) {
-      wl[i] = fast_exp2(lse_l[i] - m_use);
-      ksum += wl[i];
+      const float w = fast_exp2(lse_l[i] - m_use);
+      ksum += w;
+      wl[i] = __builtin_amdgcn_ldexpf(w, (int)e_l[i]);   // weight of the stored row
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int i = wave + W * k;           // split within the pass (wave-uniform)
+      const int i = wave + nw * k;          // split within the pass (wave-uniform)
       float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl[0]), i & 63));
 #pragma unroll
       for (int li = 1; li < LI; ++li) {
         const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl[li]), i & 63));
         w = (i >> 6) == li ? wi : w;
       }
-      if (s0 + i < S && w > 0.f) acc += w * unpack_bf16x2(raw[k]);
+      if (s0 + i < s1 && w > 0.f) acc += w * unpack_f16x2(raw[k]);
     }
     m_run = m_new;
   }
-  if constexpr (W > 1) {
+  if (W > 1 && nw > 1) {                   // uniform: every wave of the workgroup is here
     if (wave > 0) red[wave - 1][lane] = acc;
     __syncthreads();
     if (wave > 0) return;
 #pragma unroll
     for (int w = 0; w < W - 1; ++w) acc += red[w][lane];
   }
-  if (R >= n * G) return;
   ksum = wave_sum_all(ksum);
   const int tok = R / G, h = g * G + R % G;
   const float s2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;

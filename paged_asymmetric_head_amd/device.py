@@ -68,7 +68,7 @@ class DeviceInputs:
         else:
             ws, nbytes = workspace, workspace.numel() * workspace.element_size()
         fn = {"decode": B.diffkv_attn_decode, "verify": B.diffkv_attn_verify,
-              "prefill": B.diffkv_attn_prefill}[entry]
+              "prefill": B.diffkv_attn_prefill, "mixed": B.diffkv_attn_mixed}[entry]
         fn(d, self.q, self.k_cache, self.v_cache,
            self.block_table if block_table is None else block_table,
            self.seq_lens, self.q_lens, inp.window if window is None else window,

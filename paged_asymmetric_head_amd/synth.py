@@ -106,7 +106,8 @@ def make_paged_inputs(seed, *, seq_lens, q_lens, num_q_heads, num_kv_heads, page
     """Build one workload.
 
     seq_lens   list of ints, or (lo, hi) for integers uniform in [lo, hi]
-               together with batch taken from q_lens when that is a list.
+               together with batch taken from q_lens when that is a list, or
+               a list mixing ints and (lo, hi) pairs (one draw per pair).
     q_lens     int (same for every sequence) or list.
     write_align  with a window, positions before the start of the aligned
                block (of this many tokens) holding the window union's first
@@ -123,6 +124,11 @@ def make_paged_inputs(seed, *, seq_lens, q_lens, num_q_heads, num_kv_heads, page
         lo, hi = seq_lens
         L = r_len.integers(lo, hi, size=batch, endpoint=True).astype(np.int64)
         bound = hi
+    elif any(isinstance(x, tuple) for x in seq_lens):
+        L = np.array([int(r_len.integers(x[0], x[1], endpoint=True)) if isinstance(x, tuple)
+                      else int(x) for x in seq_lens], dtype=np.int64)
+        batch = L.shape[0]
+        bound = max(x[1] if isinstance(x, tuple) else int(x) for x in seq_lens)
     else:
         L = np.asarray(seq_lens, dtype=np.int64)
         batch = L.shape[0]
@@ -196,7 +202,7 @@ def make_paged_inputs(seed, *, seq_lens, q_lens, num_q_heads, num_kv_heads, page
                        max_q_len=int(n.max()), written_start=start, logical_k=lk, logical_v=lv)
 
 
-# The five workloads the path is measured and checked on.  Head counts are one
+# The workloads the path is measured and checked on.  Head counts are one
 # GPU's share of a layer; the page size, K/V format, window and sinks follow the
 # serving setups on the pages (page 128 and page 1 caches, FP8 E4M3 K/V,
 # sliding-window layers with sinks, 8-token verify, 4096-token prefill chunks
@@ -222,6 +228,13 @@ WORKLOADS = {
     # One sequence: 4096 new tokens after 26624 cached, GQA 32/2, FP8 K/V.
     "chunked_prefill": dict(seed=5, seq_lens=[30720], q_lens=4096, num_q_heads=32,
                             num_kv_heads=2, page_size=128, kv_dtype="fp8"),
+    # One serving step mixing the three kinds of sequence at the prefill
+    # chunk's head shape (GQA 32/2, page 128, FP8 K/V): the 4096-token chunk
+    # at 26K context, 4 verify blocks of 8 at 40000..50000 tokens and 32
+    # decodes at 8192..9216 tokens.
+    "mixed_batch": dict(seed=6, seq_lens=[30720] + [(40000, 50000)] * 4 + [(8192, 9216)] * 32,
+                        q_lens=[4096] + [8] * 4 + [1] * 32, num_q_heads=32, num_kv_heads=2,
+                        page_size=128, kv_dtype="fp8"),
 }
 
 

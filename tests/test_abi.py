@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("diffkv_attn_decode", "diffkv_attn_verify", "diffkv_attn_prefill",
               "diffkv_attn_workspace_bytes", "diffkv_attn_validate", "diffkv_attn_strerror",
-              "diffkv_attn_num_splits", "diffkv_kv_write"):
+              "diffkv_attn_num_splits", "diffkv_kv_write", "diffkv_attn_mixed"):
         assert n in names
 
 
@@ -55,6 +55,7 @@ def test_validate_accepts_good_descriptors(lib):
     assert B.diffkv_attn_validate(good_desc(max_q_len=1, total_q=4), B.ENTRY_DECODE) == B.OK
     assert B.diffkv_attn_validate(good_desc(kv_dtype=B.KV_FP8_E4M3, page_size=1,
                                             block_table_stride=50000), B.ENTRY_VERIFY) == B.OK
+    assert B.diffkv_attn_validate(good_desc(max_q_len=4096, total_q=4200), B.ENTRY_MIXED) == B.OK
 
 
 @pytest.mark.parametrize("field,value,entry,status", [
@@ -82,7 +83,8 @@ def test_validate_rejects(lib, field, value, entry, status):
 
 def test_validate_rejects_null_and_bad_entry(lib):
     assert lib.diffkv_attn_validate(None, 0) == B.INVALID_ARGUMENT
-    assert B.diffkv_attn_validate(good_desc(), 3) == B.INVALID_ARGUMENT
+    assert B.diffkv_attn_validate(good_desc(), 4) == B.INVALID_ARGUMENT
+    assert B.diffkv_attn_validate(good_desc(), -1) == B.INVALID_ARGUMENT
 
 
 def test_workspace_and_splits(lib):
@@ -98,6 +100,15 @@ def test_workspace_and_splits(lib):
     assert B.diffkv_attn_num_splits(d, B.ENTRY_VERIFY, 128) <= ns
     # Forced split count.
     assert B.diffkv_attn_num_splits(good_desc(force_num_splits=7), B.ENTRY_VERIFY) == 7
+    # Mixed: the split part is planned as a verify call with q_len clipped to
+    # 16, so its splits and workspace match that verify call.
+    mixed = good_desc(max_q_len=4096, total_q=4200)
+    clipped = good_desc(max_q_len=16, total_q=32)
+    assert (B.diffkv_attn_num_splits(mixed, B.ENTRY_MIXED)
+            == B.diffkv_attn_num_splits(clipped, B.ENTRY_VERIFY))
+    assert (B.diffkv_attn_workspace_bytes(mixed, B.ENTRY_MIXED)
+            == B.diffkv_attn_workspace_bytes(clipped, B.ENTRY_VERIFY))
+    assert (B.diffkv_attn_num_splits(d, B.ENTRY_MIXED) == ns)
     # Invalid descriptor -> 0 bytes.
     assert B.diffkv_attn_workspace_bytes(good_desc(batch=0), B.ENTRY_VERIFY) == 0
 

@@ -94,7 +94,7 @@ def test_grid_all_entries(case):
                             num_kv_heads=Hkv, page_size=P, kv_dtype=kv, window=W, sinks=sinks,
                             extra_pages=3, write_align=P if W > 0 else None)
     dev = DeviceInputs(inp)
-    entries = (["decode"] if n == 1 else []) + (["verify"] if n <= 16 else []) + ["prefill"]
+    entries = (["decode"] if n == 1 else []) + (["verify"] if n <= 16 else []) + ["prefill", "mixed"]
     outs = [check_call(dev, e, f"g{GRID.index(case)}/{e}") for e in entries]
     for o in outs[1:]:
         compare(to_np(o), to_np(outs[0]), "cross-entry")
