@@ -25,8 +25,9 @@ unpinned part is noted in `attention.py`.
 """
 
 from .codecs import decode_bf16, decode_e4m3fn, encode_e4m3fn
-from .attention import paged_attention, OracleResult
+from .attention import paged_attention, attention_partial, combine_partials, OracleResult
 from .kv_write import paged_kv_write
 
-__all__ = ["decode_bf16", "decode_e4m3fn", "encode_e4m3fn", "paged_attention", "OracleResult",
+__all__ = ["decode_bf16", "decode_e4m3fn", "encode_e4m3fn", "paged_attention", "attention_partial",
+           "combine_partials", "OracleResult",
            "paged_kv_write"]

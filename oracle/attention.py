@@ -41,6 +41,15 @@ Parity unpinned: the bf16 rounding pattern of a GPU output (compared within
 the tolerance only); the window and sink conventions above are readings, not
 statements of the pages.
 
+Context split ("diffbot/...", What the kernels do: split-KV; cut across
+GPUs, each GPU holding a range of a sequence's keys): `key_range` keeps only
+the keys key_lo[b] <= j < key_hi[b] of sequence b visible; `attention_partial`
+evaluates that restriction without the sink and returns each row's
+normalised output (0 where no key is visible) and its log-sum-exp (-inf
+there); `combine_partials` merges partials of disjoint key ranges by
+log-sum-exp, the sink joining the merged denominator once, which gives the
+unsplit result.
+
 Split mode (`split=k` or `split="page"`) evaluates the same rows by cutting
 each (sequence, KV head) key range into pieces, computing (max, sum, output)
 per piece and merging by log-sum-exp, as split-KV does ("diffbot/...", What
@@ -133,7 +142,7 @@ def _pieces_merged(x, V, s_h, edges):
 def paged_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens=None, *,
                     num_q_heads, num_kv_heads, kv_dtype, softmax_scale,
                     window=0, sinks=None, k_scale=1.0, v_scale=1.0,
-                    tokens=None, split=None, max_chunk_elems=1 << 22):
+                    tokens=None, split=None, key_range=None, max_chunk_elems=1 << 22):
     """Evaluate the definition above.
 
     q            uint16 [total_q, Hq, Dqk]         bf16 codes
@@ -144,6 +153,8 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens=None, *,
     q_lens       int   [B] or None (all 1)
     sinks        float [Hq] or None
     tokens       optional iterable of packed query rows to compute (default all)
+    key_range    optional (key_lo [B], key_hi [B]): only keys key_lo[b] <= j <
+                 key_hi[b] stay visible (a row may then see none)
     """
     q = np.asarray(q)
     k_cache = np.asarray(k_cache)
@@ -184,6 +195,15 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens=None, *,
             continue
         p_all = L - n + local
         lo_all = np.maximum(0, p_all - W + 1) if W > 0 else np.zeros_like(p_all)
+        if key_range is not None:
+            klo, khi = int(key_range[0][b]), int(key_range[1][b])
+            lo_all = np.maximum(lo_all, klo)
+            p_all = np.minimum(p_all, khi - 1)
+            if int((p_all - lo_all).max()) < 0:      # no token of this sequence sees a key
+                for t in local:
+                    r = row_of[int(r0 + t)]
+                    count[r, :] = 0
+                continue
 
         # Union key range of the requested tokens; only its pages are read.
         j0, j1 = int(lo_all.min()), int(p_all.max())
@@ -225,3 +245,44 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens=None, *,
                     lse[r, heads] = row_lse[a]
                     count[r, heads] = cnt[a]
     return OracleResult(out=out, lse=lse, count=count, tokens=want)
+
+
+def attention_partial(q, k_cache, v_cache, block_table, seq_lens, q_lens=None, *, key_lo, key_hi,
+                      num_q_heads, num_kv_heads, kv_dtype, softmax_scale, window=0, k_scale=1.0,
+                      v_scale=1.0, tokens=None):
+    """One key range's share of every row: the definition restricted to the keys
+    key_lo[b] <= j < key_hi[b], without the sink.  Returns an OracleResult whose
+    out is the normalised partial output (0 for a row that sees no key in the
+    range) and lse its natural log-sum-exp (-inf there)."""
+    with np.errstate(invalid="ignore", divide="ignore"):
+        res = paged_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens,
+                              num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                              kv_dtype=kv_dtype, softmax_scale=softmax_scale, window=window,
+                              sinks=None, k_scale=k_scale, v_scale=v_scale, tokens=tokens,
+                              key_range=(np.asarray(key_lo), np.asarray(key_hi)))
+    empty = res.count == 0
+    res.out[empty] = 0.0
+    res.lse[empty] = -np.inf
+    return res
+
+
+def combine_partials(outs, lses, sinks=None):
+    """Merge partials of disjoint key ranges of the same rows.
+
+    outs [S, T, Hq, Dv] normalised partial outputs, lses [S, T, Hq] their
+    log-sum-exp (-inf for a part with no key), sinks [Hq] or None.  With
+    M = max(max_s lse_s, s_h) and w_s = exp(lse_s - M):
+        out = sum_s w_s out_s / (sum_s w_s + exp(s_h - M))
+        lse = M + ln sum_s w_s          (keys only)
+    """
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    M = lses.max(axis=0)
+    if sinks is not None:
+        M = np.maximum(M, np.asarray(sinks, dtype=np.float64)[None, :])
+    w = np.where(np.isfinite(lses), np.exp(lses - M[None]), 0.0)
+    key_sum = w.sum(axis=0)
+    den = key_sum + (0.0 if sinks is None else np.exp(np.asarray(sinks, dtype=np.float64)[None, :] - M))
+    out = (w[..., None] * outs).sum(axis=0) / den[..., None]
+    with np.errstate(divide="ignore"):
+        return out, M + np.log(key_sum)
