@@ -171,6 +171,50 @@ int diffkv_attn_mixed(const diffkv_attn_desc* desc, const void* q, const void* k
                       hipStream_t stream);
 
 /*
+ * Context partials (the key-range share of a context split across GPUs, each
+ * holding a range of a sequence's keys; "diffbot/MiMo-V2.6-Flash-RL-FP8KV-
+ * W4A8-2x-RTX-PRO-6000", What the kernels do: split-KV, here cut across key
+ * ranges).  Computes, for every row of a verify-shaped call (max_q_len <= 16),
+ * the attention above restricted to the keys key_lo[b] <= j < key_hi[b] of
+ * its sequence, without the sink:
+ *   out_part  fp32 [total_q, Hq, 128]: sum over those keys of p_j V_j / sum p_j
+ *             (v_scale applied), 0 for a row that sees no key in the range
+ *   lse_part  fp32 [total_q, Hq]: natural log-sum-exp of those keys' logits,
+ *             -inf for a row that sees none
+ *   key_lo, key_hi  int32 [batch] device arrays, or NULL for 0 / no bound
+ * Only block-table entries of pages holding a key in the range are read, so
+ * a caller holding part of a sequence may leave the others invalid.  The
+ * workspace is the verify entry's: diffkv_attn_workspace_bytes(desc,
+ * DIFFKV_ENTRY_VERIFY).  Other arguments, ownership and errors as for
+ * attention; count_out counts the keys in range.  Partials of disjoint ranges
+ * covering every visible key, merged by diffkv_attn_combine with the sinks,
+ * give the attention output.
+ */
+int diffkv_attn_partial(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                        const int32_t* q_lens, const int32_t* key_lo, const int32_t* key_hi,
+                        int32_t window, float k_scale, float v_scale, float softmax_scale,
+                        float* out_part, float* lse_part, int32_t* count_out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Merge of context partials for `rows` = total_q * num_q_heads rows (row r is
+ * query head r % num_q_heads):
+ *   out_parts  fp32 [num_parts, rows, 128], lse_parts fp32 [num_parts, rows]
+ *              (diffkv_attn_partial's outputs, stacked; -inf marks a part
+ *              with no key for that row)
+ *   sinks      fp32 [num_q_heads] or NULL, joining the merged denominator once
+ *   out        bf16 [rows, 128]: sum_s w_s out_s / (sum_s w_s + e^(sink - M)),
+ *              w_s = e^(lse_s - M), M = max(lse_s, sink); 0 if nothing is visible
+ *   lse_out    fp32 [rows] (keys only) or NULL
+ * num_parts in [1, 64] (DIFFKV_UNSUPPORTED beyond); rows a positive multiple
+ * of num_q_heads.  Parts are summed in index order (deterministic).
+ */
+int diffkv_attn_combine(int32_t num_parts, int32_t rows, int32_t num_q_heads,
+                        const float* out_parts, const float* lse_parts, const float* sinks,
+                        void* out, float* lse_out, hipStream_t stream);
+
+/*
  * Paged KV write: stores the new tokens' K and V rows into their cache slots,
  * the step before attention reads them ("diffbot/MiMo-V2.6-Flash-RL-FP8KV-
  * W4A8-2x-RTX-PRO-6000", intro: an E4M3 KV cache with per-tensor scales;
@@ -218,9 +262,9 @@ int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry);
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window);
 
 /* Profiling hook.  Arms two caller-created HIP events for the next
- * decode/verify/prefill/mixed/kv_write call made on this host thread: that
- * call's first main kernel (not the split merge; for mixed, the split-KV
- * kernel) is dispatched with them as its
+ * decode/verify/prefill/mixed/partial/combine/kv_write call made on this host
+ * thread: that call's first main kernel (not the split merge; for mixed, the
+ * split-KV kernel) is dispatched with them as its
  * start and stop events (hipExtLaunchKernel), so hipEventElapsedTime(start,
  * stop) is that kernel's execution time.  The hook disarms after one call;
  * passing two NULLs disarms it.  Returns DIFFKV_INVALID_ARGUMENT if exactly

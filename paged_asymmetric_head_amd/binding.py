@@ -56,6 +56,13 @@ def load_library():
         fn.restype = ctypes.c_int
     lib.diffkv_kv_write.argtypes = [ctypes.POINTER(AttnDesc)] + [ctypes.c_void_p] * 7 + [
         ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+    lib.diffkv_attn_partial.argtypes = [ctypes.POINTER(AttnDesc)] + [ctypes.c_void_p] * 8 + [
+        ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.diffkv_attn_partial.restype = ctypes.c_int
+    lib.diffkv_attn_combine.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32] + [
+        ctypes.c_void_p] * 6
+    lib.diffkv_attn_combine.restype = ctypes.c_int
     lib.diffkv_kv_write.restype = ctypes.c_int
     lib.diffkv_attn_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int]
     lib.diffkv_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -182,3 +189,24 @@ def diffkv_kv_write(desc, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
                     k_scale=1.0, v_scale=1.0, stream=None):
     prepared_kv_write(desc, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_lens,
                       k_scale, v_scale, stream)()
+
+
+def diffkv_attn_partial(desc, q, k_cache, v_cache, block_table, seq_lens, q_lens, key_lo, key_hi,
+                        window, k_scale, v_scale, softmax_scale, out_part, lse_part,
+                        count_out=None, workspace=None, workspace_bytes=0, stream=None):
+    status = load_library().diffkv_attn_partial(
+        ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(q_lens), _ptr(key_lo), _ptr(key_hi), int(window), float(k_scale),
+        float(v_scale), float(softmax_scale), _ptr(out_part), _ptr(lse_part), _ptr(count_out),
+        _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if status != OK:
+        raise DiffKVError(f"diffkv_attn_partial: {diffkv_attn_strerror(status)} (status {status})")
+
+
+def diffkv_attn_combine(num_parts, rows, num_q_heads, out_parts, lse_parts, sinks, out,
+                        lse_out=None, stream=None):
+    status = load_library().diffkv_attn_combine(
+        int(num_parts), int(rows), int(num_q_heads), _ptr(out_parts), _ptr(lse_parts),
+        _ptr(sinks), _ptr(out), _ptr(lse_out), _stream(stream))
+    if status != OK:
+        raise DiffKVError(f"diffkv_attn_combine: {diffkv_attn_strerror(status)} (status {status})")

@@ -14,6 +14,7 @@
 #include "split_attn.hpp"
 #include "prefill_attn.hpp"
 #include "kv_write.hpp"
+#include "combine.hpp"
 
 using namespace diffkv;
 
@@ -148,14 +149,24 @@ hipError_t launch_fill(int32_t* p, size_t n, hipStream_t stream) {
                          args, 0, stream);
 }
 
+// Context partials (part_out set) run as a verify call restricted to the key
+// ranges [key_lo[b], key_hi[b]), without sinks, writing fp32 partial rows.
+struct PartialMode {
+  const int32_t* key_lo = nullptr;
+  const int32_t* key_hi = nullptr;
+  float* part_out = nullptr;
+};
+
 int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k_cache,
               const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
               const int32_t* q_lens, int32_t window, const float* sinks, float k_scale,
               float v_scale, float softmax_scale, void* out, float* lse_out, int32_t* count_out,
-              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+              void* workspace, size_t workspace_bytes, hipStream_t stream,
+              const PartialMode& pm = PartialMode()) {
   const int st = validate_desc(d, entry);
   if (st != DIFFKV_OK) return st;
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return DIFFKV_INVALID_ARGUMENT;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !(out || pm.part_out))
+    return DIFFKV_INVALID_ARGUMENT;
   if (!q_lens && d->max_q_len != 1) return DIFFKV_INVALID_ARGUMENT;
   const bool fp8 = d->kv_dtype == DIFFKV_KV_FP8_E4M3;
   const float ks = fp8 ? k_scale : 1.f;
@@ -192,6 +203,9 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
   a.window = window;
   a.q_lo = 1;
   a.q_hi = INT32_MAX;
+  a.key_lo = pm.key_lo;
+  a.key_hi = pm.key_hi;
+  a.part_out = pm.part_out;
   a.scale_log2 = softmax_scale * ks * kLog2e;
   a.v_scale = vs;
 
@@ -318,6 +332,37 @@ int diffkv_kv_write(const diffkv_attn_desc* desc, const void* k_new, const void*
                     hipStream_t stream) {
   return run_kv_write(desc, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_lens,
                       k_scale, v_scale, stream);
+}
+
+int diffkv_attn_partial(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                        const int32_t* q_lens, const int32_t* key_lo, const int32_t* key_hi,
+                        int32_t window, float k_scale, float v_scale, float softmax_scale,
+                        float* out_part, float* lse_part, int32_t* count_out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  if (out_part == nullptr || lse_part == nullptr) return DIFFKV_INVALID_ARGUMENT;
+  PartialMode pm;
+  pm.key_lo = key_lo;
+  pm.key_hi = key_hi;
+  pm.part_out = out_part;
+  return run_entry(DIFFKV_ENTRY_VERIFY, desc, q, k_cache, v_cache, block_table, seq_lens, q_lens,
+                   window, nullptr, k_scale, v_scale, softmax_scale, nullptr, lse_part, count_out,
+                   workspace, workspace_bytes, stream, pm);
+}
+
+int diffkv_attn_combine(int32_t num_parts, int32_t rows, int32_t num_q_heads,
+                        const float* out_parts, const float* lse_parts, const float* sinks,
+                        void* out, float* lse_out, hipStream_t stream) {
+  if (num_parts < 1 || rows < 1 || num_q_heads < 1 || rows % num_q_heads != 0)
+    return DIFFKV_INVALID_ARGUMENT;
+  if (num_parts > kMaxCombineParts) return DIFFKV_UNSUPPORTED;
+  if (!out_parts || !lse_parts || !out) return DIFFKV_INVALID_ARGUMENT;
+  CombineArgs a{out_parts, lse_parts, sinks, static_cast<uint16_t*>(out), lse_out,
+                num_parts, rows, num_q_heads};
+  void* args[] = {&a};
+  const hipError_t e = launch_main(reinterpret_cast<const void*>(&combine_kernel),
+                                   dim3((unsigned)((rows + 3) / 4)), dim3(256), args, stream);
+  return e == hipSuccess ? DIFFKV_OK : DIFFKV_HIP_ERROR;
 }
 
 int diffkv_attn_mixed(const diffkv_attn_desc* desc, const void* q, const void* k_cache,

@@ -184,4 +184,13 @@ __device__ __forceinline__ void qtile_key_range(int L, int n, int G, int qt, int
   kv_hi = p_hi + 1;
 }
 
+// The same range cut to the keys [klo, khi) (a context partial's share); it
+// may come out empty (hi <= lo).
+__device__ __forceinline__ void pair_key_range(int L, int n, int G, int qt, int rows, int window,
+                                               int klo, int khi, int& kv_lo, int& kv_hi) {
+  qtile_key_range(L, n, G, qt, rows, window, kv_lo, kv_hi);
+  kv_lo = max(kv_lo, klo);
+  kv_hi = min(kv_hi, khi);
+}
+
 }  // namespace diffkv

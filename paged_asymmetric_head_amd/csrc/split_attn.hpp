@@ -50,6 +50,13 @@ struct SplitArgs {
   int slots;          // balanced plan: target chunks per KV head (one resident round)
   int force_splits;   // > 0: every (sequence, query tile) takes exactly this many chunks
   int chunk_bound;    // chunk ids stay below this (the workspace holds that many)
+  // Context partials: keys outside [key_lo[b], key_hi[b]) stay invisible
+  // (NULL: no bound), and with part_out set the rows are written as fp32
+  // normalised outputs (0 for a row that sees no key) with their natural
+  // log-sum-exp in lse_out (-inf there); the sink is not applied.
+  const int32_t* key_lo;
+  const int32_t* key_hi;
+  float* part_out;
   int q_lo, q_hi;     // this launch takes the sequences with q_lo <= q_len <= q_hi
   float scale_log2;   // softmax_scale * k_scale * log2(e)
   float v_scale;      // v_scale for FP8 caches, 1 for bf16
@@ -83,62 +90,69 @@ struct SplitPlanner {
   const SplitArgs& a;
   int C = 0;            // tiles per chunk; 0 with forced splits
   int L0 = 0, n0 = 0;   // this lane's sequence (b = lane) of the first pass
+  int lo0 = 0, hi0 = 0; // its key bounds
 
   __device__ __forceinline__ explicit SplitPlanner(const SplitArgs& args) : a(args) {}
 
-  // Lengths of sequence b0 + lane (new tokens 0 past the batch).
-  __device__ __forceinline__ void load(int b0, int& L, int& n) const {
+  // Lengths and key bounds of sequence b0 + lane (new tokens 0 past the batch).
+  __device__ __forceinline__ void load(int b0, int& L, int& n, int& klo, int& khi) const {
     const int b = b0 + lane_id();
     L = 0;
     n = 0;
+    klo = 0;
+    khi = INT32_MAX;
     if (b < a.batch) {
       L = a.seq_lens[b];
       n = a.q_lens ? a.q_lens[b] : 1;
+      if (a.key_lo) klo = a.key_lo[b];
+      if (a.key_hi) khi = a.key_hi[b];
     }
   }
   __device__ __forceinline__ int qtiles(int n) const {
     return n >= a.q_lo && n <= a.q_hi ? min((n * a.group + ROWS - 1) / ROWS, a.n_qtiles) : 0;
   }
-  __device__ __forceinline__ int tiles(int L, int n, int qt) const {
+  __device__ __forceinline__ int tiles(int L, int n, int qt, int klo, int khi) const {
     int lo, hi;
-    qtile_key_range(L, n, a.group, qt, ROWS, a.window, lo, hi);
-    return (hi + kTileKeys - 1) / kTileKeys - lo / kTileKeys;
+    pair_key_range(L, n, a.group, qt, ROWS, a.window, klo, khi, lo, hi);
+    return hi > lo ? (hi + kTileKeys - 1) / kTileKeys - lo / kTileKeys : 0;
   }
-  __device__ __forceinline__ int chunks(int L, int n, int qt) const {
-    return a.force_splits > 0 ? a.force_splits : (tiles(L, n, qt) + C - 1) / C;
+  // At least one chunk per pair, so a pair with no key in range still
+  // writes its rows.
+  __device__ __forceinline__ int chunks(int L, int n, int qt, int klo, int khi) const {
+    return a.force_splits > 0 ? a.force_splits : max(1, (tiles(L, n, qt, klo, khi) + C - 1) / C);
   }
   // Chunks of all query tiles of a sequence (0 for one this launch skips).
-  __device__ __forceinline__ int seq_chunks(int L, int n) const {
+  __device__ __forceinline__ int seq_chunks(int L, int n, int klo, int khi) const {
     int k = 0;
     const int nq = qtiles(n);
-    for (int qt = 0; qt < nq; ++qt) k += chunks(L, n, qt);
+    for (int qt = 0; qt < nq; ++qt) k += chunks(L, n, qt, klo, khi);
     return k;
   }
 
   __device__ __forceinline__ void init() {
-    load(0, L0, n0);
+    load(0, L0, n0, lo0, hi0);
     if (a.force_splits > 0) return;
     int T = 0;
     for (int b0 = 0; b0 < a.batch; b0 += 64) {
-      int L = L0, n = n0;
-      if (b0 > 0) load(b0, L, n);
+      int L = L0, n = n0, klo = lo0, khi = hi0;
+      if (b0 > 0) load(b0, L, n, klo, khi);
       const int nq = qtiles(n);
-      for (int qt = 0; qt < nq; ++qt) T += tiles(L, n, qt);
+      for (int qt = 0; qt < nq; ++qt) T += tiles(L, n, qt, klo, khi);
     }
     T = wave_sum_int(T);
     C = max(kMinTilesPerSplit, (T + a.slots - 1) / a.slots);
   }
 
-  // The pair and chunk of chunk id w, with the sequence's lengths and its
-  // first packed query row; false when w is past the last chunk.
+  // The pair and chunk of chunk id w, with the sequence's lengths, key
+  // bounds and first packed query row; false when w is past the last chunk.
   __device__ __forceinline__ bool find(int w, int& b, int& qt, int& c, int& base, int& k, int& L_b,
-                                       int& n_b, int& r0) const {
+                                       int& n_b, int& klo_b, int& khi_b, int& r0) const {
     int before = 0;                           // chunks of the earlier passes
     int rows_before = 0;                      // new tokens of the earlier passes
     for (int b0 = 0; b0 < a.batch; b0 += 64) {
-      int L = L0, n = n0;
-      if (b0 > 0) load(b0, L, n);
-      const int kb = seq_chunks(L, n);
+      int L = L0, n = n0, klo = lo0, khi = hi0;
+      if (b0 > 0) load(b0, L, n, klo, khi);
+      const int kb = seq_chunks(L, n, klo, khi);
       // Inclusive prefix sums over the lanes (chunks, and new tokens for the
       // packed row start).
       int incl = kb, nincl = n;
@@ -161,10 +175,12 @@ struct SplitPlanner {
         base = before + read_lane(incl - kb, owner);
         L_b = read_lane(L, owner);
         n_b = read_lane(n, owner);
+        klo_b = read_lane(klo, owner);
+        khi_b = read_lane(khi, owner);
         r0 = a.q_lens ? rows_before + read_lane(nincl - n, owner) : b;
         const int nq = qtiles(n_b);
         for (qt = 0; qt < nq; ++qt) {
-          k = chunks(L_b, n_b, qt);
+          k = chunks(L_b, n_b, qt, klo_b, khi_b);
           if (w < base + k) {
             c = w - base;
             return true;
@@ -200,32 +216,48 @@ void split_attn_kernel(const SplitArgs a) {
 
   // Which pair and chunk: one chunk per pair when DIRECT (grid.x = pairs),
   // else the balanced plan.
-  int b, qt, c = 0, base = 0, k = 1, L, n, r0;
+  int b, qt, c = 0, base = 0, k = 1, L, n, klo, khi, r0;
   if constexpr (DIRECT) {
     b = blockIdx.x / a.n_qtiles;
     qt = blockIdx.x % a.n_qtiles;
     L = a.seq_lens[b];
     n = a.q_lens ? a.q_lens[b] : 1;
+    klo = a.key_lo ? a.key_lo[b] : 0;
+    khi = a.key_hi ? a.key_hi[b] : INT32_MAX;
     r0 = -1;                                  // summed below, after the loads are out
   } else {
     SplitPlanner<ROWS> plan(a);
     plan.init();
-    if (!plan.find(blockIdx.x, b, qt, c, base, k, L, n, r0) || base + c >= a.chunk_bound) return;
+    if (!plan.find(blockIdx.x, b, qt, c, base, k, L, n, klo, khi, r0) || base + c >= a.chunk_bound)
+      return;
     // The pair's first chunk records where the merge finds the pair.
     if (c == 0 && tid == 0) a.pair_chunks[(size_t)b * a.n_qtiles + qt] = i32x2{base, k};
   }
   if (qt * ROWS >= n * G || n < a.q_lo || n > a.q_hi) return;
   // A pair of one chunk writes its output here; the merge skips it.
   const bool direct = DIRECT || k == 1;
-  int kv_lo, kv_hi, t_begin, t_end;
-  qtile_key_range(L, n, G, qt, ROWS, a.window, kv_lo, kv_hi);
-  split_tiles(kv_lo, kv_hi, k, c, t_begin, t_end);
+  int kv_lo, kv_hi, t_begin = 0, t_end = 0;
+  pair_key_range(L, n, G, qt, ROWS, a.window, klo, khi, kv_lo, kv_hi);
+  if (kv_hi > kv_lo) split_tiles(kv_lo, kv_hi, k, c, t_begin, t_end);
   // Partial row of this chunk for row r of the tile.
   const size_t prow0 = ((size_t)(base + c) * a.hkv + g) * ROWS;
   if (t_begin >= t_end) {
-    // An empty chunk (forced splits only) still marks its rows (log-sum-exp
-    // -inf) so the merge can read every chunk of the pair.
-    if (!direct && tid < ROWS && qt * ROWS + tid < n * G) a.part_lse[prow0 + tid] = f32x2{-INFINITY, 0.f};
+    // An empty chunk (forced splits, or a key range the tile's rows do not
+    // reach) still marks its rows: log-sum-exp -inf for the merge, or, when
+    // it is the pair's only chunk, the empty rows of a context partial.
+    const bool row = tid < ROWS && qt * ROWS + tid < n * G;
+    if (!direct) {
+      if (row) a.part_lse[prow0 + tid] = f32x2{-INFINITY, 0.f};
+    } else if (a.part_out) {                  // uniform: whole waves take this branch
+      if constexpr (DIRECT) r0 = seq_row_start(a.q_lens, b);
+      if (row) {
+        const int R = qt * ROWS + tid;
+        const size_t out_row = (size_t)(r0 + R / G) * a.hq + g * G + R % G;
+        for (int d = 0; d < kHeadDimV; d += 4)
+          *reinterpret_cast<f32x4*>(a.part_out + out_row * kHeadDimV + d) = f32x4{0.f, 0.f, 0.f, 0.f};
+        a.lse_out[out_row] = -INFINITY;
+      }
+    }
     return;
   }
 
@@ -252,8 +284,8 @@ void split_attn_kernel(const SplitArgs a) {
   const int tok = row_ok ? R / G : 0;
   const int h = g * G + (row_ok ? R % G : 0);
   const int p_row = L - n + tok;
-  const int lo_row = a.window > 0 ? max(0, p_row - a.window + 1) : 0;
-  const int hi_row = row_ok ? p_row : -1;     // empty interval for padding rows
+  const int lo_row = max(a.window > 0 ? max(0, p_row - a.window + 1) : 0, klo);
+  const int hi_row = row_ok ? min(p_row, khi - 1) : -1;   // empty interval for padding rows
 
   // Q^T operand: contraction chunk c carries dims 32c + 8*grp .. +7.
   u32x4 qreg[6];
@@ -277,8 +309,8 @@ void split_attn_kernel(const SplitArgs a) {
   // results stay in their own lanes and are never written.
   const int r_first = qt * ROWS;
   const int r_last = min(n * G, r_first + ROWS) - 1;
-  const int p_first = L - n + r_first / G;
-  const int lo_last = a.window > 0 ? max(0, L - n + r_last / G - a.window + 1) : 0;
+  const int p_first = min(L - n + r_first / G, khi - 1);
+  const int lo_last = max(a.window > 0 ? max(0, L - n + r_last / G - a.window + 1) : 0, klo);
   const float scale = a.scale_log2;   // > 0 (checked on the host)
 
   // One online-softmax update per tile: the S^T tiles of all this wave's
@@ -436,9 +468,16 @@ void split_attn_kernel(const SplitArgs a) {
       const float al = fast_exp2(m - M2);
       coef = al / (l * al + fast_exp2(s2 - M2));
     } else {
-      coef = 1.f / l;
+      coef = l > 0.f ? 1.f / l : 0.f;         // l == 0 only for a context partial's empty row
     }
     coef *= a.v_scale;
+    if (a.part_out) {
+      float* op = a.part_out + out_row * kHeadDimV + 4 * grp;
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) *reinterpret_cast<f32x4*>(op + 16 * nn) = o[nn] * coef;
+      if (grp == 0) a.lse_out[out_row] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+      return;
+    }
     uint16_t* op = a.out + out_row * kHeadDimV + 4 * grp;
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn) {
@@ -582,10 +621,16 @@ __global__ __launch_bounds__(64 * W) void split_merge_kernel(const SplitArgs a) 
   const int tok = R / G, h = g * G + R % G;
   const float s2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
   const float Mt = fmaxf(m_run, s2);
-  const float f = fast_exp2(m_run - Mt);
-  const float den = ksum * f + (a.sinks ? fast_exp2(s2 - Mt) : 0.f);
-  const float coef = a.v_scale * f / den;
+  const float Mt_use = Mt == -INFINITY ? 0.f : Mt;   // a context partial's row with no key
+  const float f = fast_exp2(m_run - Mt_use);
+  const float den = ksum * f + (a.sinks ? fast_exp2(s2 - Mt_use) : 0.f);
+  const float coef = den > 0.f ? a.v_scale * f / den : 0.f;
   const size_t out_row = (size_t)(r0 + tok) * a.hq + h;
+  if (a.part_out) {
+    *reinterpret_cast<f32x2*>(a.part_out + out_row * kHeadDimV + 2 * lane) = acc * coef;
+    if (lane == 0) a.lse_out[out_row] = ksum > 0.f ? (m_run + log2f(ksum)) * kLn2 : -INFINITY;
+    return;
+  }
   *reinterpret_cast<uint32_t*>(a.out + out_row * kHeadDimV + 2 * lane) = pack_bf16x2(acc.x * coef, acc.y * coef);
   if (a.lse_out && lane == 0) a.lse_out[out_row] = (m_run + log2f(ksum)) * kLn2;
 }

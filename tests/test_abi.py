@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("diffkv_attn_decode", "diffkv_attn_verify", "diffkv_attn_prefill",
               "diffkv_attn_workspace_bytes", "diffkv_attn_validate", "diffkv_attn_strerror",
-              "diffkv_attn_num_splits", "diffkv_kv_write", "diffkv_attn_mixed"):
+              "diffkv_attn_num_splits", "diffkv_kv_write", "diffkv_attn_mixed",
+              "diffkv_attn_partial", "diffkv_attn_combine"):
         assert n in names
 
 
@@ -154,3 +155,23 @@ def test_kv_write_rejects_before_touching_the_gpu(lib):
     fp8 = good_desc(kv_dtype=B.KV_FP8_E4M3)
     for ks, vs in ((0.0, 1.0), (1.0, -2.0), (float("nan"), 1.0), (1.0, float("inf"))):
         assert call(fp8, ks=ks, vs=vs) == B.INVALID_ARGUMENT, (ks, vs)
+
+
+def test_partial_and_combine_reject_before_touching_the_gpu(lib):
+    fake = 256                      # never dereferenced: every case fails its checks first
+    d = good_desc()
+    fn = lib.diffkv_attn_partial
+    # out_part / lse_part missing
+    assert fn(ctypes.byref(d), *[fake] * 8, 0, 1.0, 1.0, 1.0, None, fake, None, None, 0, None) \
+        == B.INVALID_ARGUMENT
+    assert fn(ctypes.byref(d), *[fake] * 8, 0, 1.0, 1.0, 1.0, fake, None, None, None, 0, None) \
+        == B.INVALID_ARGUMENT
+    # verify-shaped only
+    d17 = good_desc(max_q_len=17)
+    assert fn(ctypes.byref(d17), *[fake] * 8, 0, 1.0, 1.0, 1.0, fake, fake, None, None, 0, None) \
+        == B.INVALID_ARGUMENT
+    c = lib.diffkv_attn_combine
+    assert c(0, 8, 4, fake, fake, None, fake, None, None) == B.INVALID_ARGUMENT
+    assert c(2, 10, 4, fake, fake, None, fake, None, None) == B.INVALID_ARGUMENT   # rows % Hq
+    assert c(65, 8, 4, fake, fake, None, fake, None, None) == B.UNSUPPORTED
+    assert c(2, 8, 4, None, fake, None, fake, None, None) == B.INVALID_ARGUMENT
