@@ -20,8 +20,11 @@ steps alone (HIP events around the K calls, no per-call instrumentation).
 calls has the library's dispatch stamp each main kernel with HIP events
 (diffkv_attn_profile_next_call); their mean is the kernel's duration.
 `cpu_baseline` times the FP64 oracle on the host on a bounded sample.
-`extra` carries the other workloads measured the same way, and the paged KV
-write (diffkv_kv_write) on the decode and prefill token counts.
+`extra` carries the other workloads measured the same way (mixed_batch: one
+serving step mixing a prefill chunk, verify blocks and decodes), the paged KV
+write (diffkv_kv_write) on the decode and prefill token counts, and one GPU's
+share of a two-way context split of the decode workload (diffkv_attn_partial
+over half of every sequence's keys, and the diffkv_attn_combine merge).
 """
 
 import argparse
@@ -269,6 +272,59 @@ def measure_kv_write(name, steps, warmup, events, target_bytes=1 << 30):
                          "work_per_launch": nbytes}}
 
 
+def measure_context_split(steps, warmup, events, parts=2, target_bytes=1 << 30):
+    """One GPU's share of a context split of the batched-decode workload: the
+    partial over the first of `parts` page-aligned key ranges of every
+    sequence (through a block table holding only that range's pages), and the
+    owner's combine of `parts` partials."""
+    import numpy as np
+    import torch
+    from paged_asymmetric_head_amd import binding as B
+    from paged_asymmetric_head_amd.device import DeviceInputs, _to_device
+    from paged_asymmetric_head_amd.synth import workload
+
+    inp = workload("batched_decode")
+    dev = DeviceInputs(inp)
+    P = inp.page_size
+    lo = np.zeros(inp.batch, dtype=np.int32)
+    hi = np.array([min(int(L), (-(-int(L) // P) // parts) * P) for L in inp.seq_lens], dtype=np.int32)
+    bt = np.full_like(inp.block_table, -1)
+    for b in range(inp.batch):
+        bt[b, :(int(hi[b]) + P - 1) // P] = inp.block_table[b, :(int(hi[b]) + P - 1) // P]
+    bt_d = _to_device(bt.astype(np.int32), "cuda")
+    lo_d, hi_d = _to_device(lo, "cuda"), _to_device(hi, "cuda")
+    pool = dev.k_cache.numel() * dev.k_cache.element_size() + dev.v_cache.numel() * dev.v_cache.element_size()
+    layers = max(1, min(16, math.ceil(target_bytes / pool)))
+    caches = [(dev.k_cache, dev.v_cache)] + [(dev.k_cache.clone(), dev.v_cache.clone())
+                                             for _ in range(layers - 1)]
+    rows = inp.total_q * inp.num_q_heads
+    out_parts = torch.zeros((parts, rows, 128), dtype=torch.float32, device="cuda")
+    lse_parts = torch.zeros((parts, rows), dtype=torch.float32, device="cuda")
+    d = dev.desc("verify")
+    ws, nbytes = dev.workspace_for("verify")
+    stream = torch.cuda.current_stream().cuda_stream
+    calls = [B.prepared_partial(d, dev.q, k, v, bt_d, dev.seq_lens, dev.q_lens, lo_d, hi_d,
+                                inp.window, inp.k_scale, inp.v_scale, inp.softmax_scale,
+                                out_parts[0], lse_parts[0], None, ws, nbytes, stream)
+             for k, v in caches]
+    total_ms, _, kern = time_calls(calls, steps, warmup, events, stream)
+    out = torch.empty((rows, 128), dtype=torch.bfloat16, device="cuda")
+    comb = [B.prepared_combine(parts, rows, inp.num_q_heads, out_parts, lse_parts, dev.sinks, out,
+                               None, stream)]
+    c_total, _, c_kern = time_calls(comb, steps, warmup, events, stream)
+    kv_bytes = int(hi.astype(np.int64).sum() - lo.sum()) * inp.num_kv_heads * (192 + 128) * 2
+    ms = sum(kern) / len(kern)
+    achieved = kv_bytes / (ms * 1e-3) / 1e9
+    return {"entry": "partial+combine", "workload": "batched_decode", "parts": parts,
+            "partial_ms_per_step": round(total_ms / steps, 5),
+            "combine_ms_per_step": round(c_total / steps, 5),
+            "combine_kernel_ms": round(sum(c_kern) / len(c_kern), 5), "layers": layers,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "split_attn_kernel (context partial)", "kernel_ms": round(ms, 5),
+                         "work_per_launch": kv_bytes}}
+
+
 COPY_BYTES = 256 << 20
 
 
@@ -478,6 +534,9 @@ def main():
             print(f"[bench] {other}: generating and measuring", file=sys.stderr, flush=True)
             extra[other] = measure_kv_write(other, args.extra_steps, 5, events)
             torch.cuda.empty_cache()
+        print("[bench] context_split_decode: generating and measuring", file=sys.stderr, flush=True)
+        extra["context_split_decode"] = measure_context_split(args.extra_steps, 5, events)
+        torch.cuda.empty_cache()
         result["extra"] = extra
     if args.copy_calibration:
         copy_calibration()

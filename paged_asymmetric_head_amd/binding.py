@@ -191,22 +191,41 @@ def diffkv_kv_write(desc, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
                       k_scale, v_scale, stream)()
 
 
-def diffkv_attn_partial(desc, q, k_cache, v_cache, block_table, seq_lens, q_lens, key_lo, key_hi,
-                        window, k_scale, v_scale, softmax_scale, out_part, lse_part,
-                        count_out=None, workspace=None, workspace_bytes=0, stream=None):
-    status = load_library().diffkv_attn_partial(
-        ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-        _ptr(seq_lens), _ptr(q_lens), _ptr(key_lo), _ptr(key_hi), int(window), float(k_scale),
-        float(v_scale), float(softmax_scale), _ptr(out_part), _ptr(lse_part), _ptr(count_out),
-        _ptr(workspace), int(workspace_bytes), _stream(stream))
-    if status != OK:
-        raise DiffKVError(f"diffkv_attn_partial: {diffkv_attn_strerror(status)} (status {status})")
+def _prepared(name, args, keep):
+    fn = getattr(load_library(), name)
+
+    def call():
+        status = fn(*args)
+        if status != OK:
+            raise DiffKVError(f"{name}: {diffkv_attn_strerror(status)} (status {status})")
+    call.keep_alive = keep
+    return call
 
 
-def diffkv_attn_combine(num_parts, rows, num_q_heads, out_parts, lse_parts, sinks, out,
-                        lse_out=None, stream=None):
-    status = load_library().diffkv_attn_combine(
-        int(num_parts), int(rows), int(num_q_heads), _ptr(out_parts), _ptr(lse_parts),
-        _ptr(sinks), _ptr(out), _ptr(lse_out), _stream(stream))
-    if status != OK:
-        raise DiffKVError(f"diffkv_attn_combine: {diffkv_attn_strerror(status)} (status {status})")
+def prepared_partial(desc, q, k_cache, v_cache, block_table, seq_lens, q_lens, key_lo, key_hi,
+                     window, k_scale, v_scale, softmax_scale, out_part, lse_part, count_out=None,
+                     workspace=None, workspace_bytes=0, stream=None):
+    """Like prepared_call, for diffkv_attn_partial."""
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(seq_lens), _ptr(q_lens), _ptr(key_lo), _ptr(key_hi), int(window), float(k_scale),
+            float(v_scale), float(softmax_scale), _ptr(out_part), _ptr(lse_part), _ptr(count_out),
+            _ptr(workspace), int(workspace_bytes), _stream(stream))
+    return _prepared("diffkv_attn_partial", args,
+                     (desc, q, k_cache, v_cache, block_table, seq_lens, q_lens, key_lo, key_hi,
+                      out_part, lse_part, count_out, workspace))
+
+
+def prepared_combine(num_parts, rows, num_q_heads, out_parts, lse_parts, sinks, out,
+                     lse_out=None, stream=None):
+    """Like prepared_call, for diffkv_attn_combine."""
+    args = (int(num_parts), int(rows), int(num_q_heads), _ptr(out_parts), _ptr(lse_parts),
+            _ptr(sinks), _ptr(out), _ptr(lse_out), _stream(stream))
+    return _prepared("diffkv_attn_combine", args, (out_parts, lse_parts, sinks, out, lse_out))
+
+
+def diffkv_attn_partial(*args, **kwargs):
+    prepared_partial(*args, **kwargs)()
+
+
+def diffkv_attn_combine(*args, **kwargs):
+    prepared_combine(*args, **kwargs)()
