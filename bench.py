@@ -57,7 +57,10 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="batched_decode", choices=sorted(ENTRY_OF))
+    ap.add_argument("--workload", default="batched_decode",
+                    choices=sorted(ENTRY_OF) + sorted(KV_WRITE_OF) + ["context_split_decode"],
+                    help="attention workload for the headline line; a KV-write or context-split "
+                         "name prints that measurement's own line instead")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -146,7 +149,10 @@ def kernel_source_sha():
         with open(path, encoding="utf-8") as f:
             h.update(os.path.basename(path).encode())
             h.update(_code_only(f.read()).encode())
-    flags = [c for c in command("OUT") if not os.path.isabs(c) and c != "OUT" and "hipcc" not in c]
+    # Flags only: the compiler path, the output and the include directories
+    # (which name the checkout's location) are left out.
+    flags = [c for c in command("OUT")
+             if not os.path.isabs(c) and c != "OUT" and "hipcc" not in c and not c.startswith("-I")]
     h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
@@ -495,6 +501,13 @@ def main():
     events = HipEvents()
 
     name = args.workload
+    if name not in ENTRY_OF:
+        print(f"[bench] {name}: generating and measuring", file=sys.stderr, flush=True)
+        res = (measure_kv_write(name, args.steps, args.warmup, events) if name in KV_WRITE_OF
+               else measure_context_split(args.steps, args.warmup, events))
+        print(json.dumps({"workload": name, "steps": args.steps, "warmup": args.warmup,
+                          "kernel_source_sha": sha, **res}), flush=True)
+        return
     print(f"[bench] {name}: generating and measuring", file=sys.stderr, flush=True)
     m = measure(name, args.steps, args.warmup, events)
     head = summary(m, sha, name)
