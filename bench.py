@@ -21,7 +21,8 @@ calls has the library's dispatch stamp each main kernel with HIP events
 (diffkv_attn_profile_next_call); their mean is the kernel's duration.
 `cpu_baseline` times the FP64 oracle on the host on a bounded sample.
 `extra` carries the other workloads measured the same way (mixed_batch: one
-serving step mixing a prefill chunk, verify blocks and decodes), the paged KV
+serving step mixing a prefill chunk, verify blocks and decodes;
+batched_decode_sym: the decode batch with symmetric 128/128 heads), the paged KV
 write (diffkv_kv_write) on the decode and prefill token counts, and one GPU's
 share of a two-way context split of the decode workload (diffkv_attn_partial
 over half of every sequence's keys, and the diffkv_attn_combine merge).
@@ -46,7 +47,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ENTRY_OF = {"tiny_decode": "decode", "batched_decode": "decode", "verify_long": "verify",
             "swa_sinks_fp8_p1": "verify", "swa_sinks_fp8_p128": "verify",
-            "chunked_prefill": "prefill", "mixed_batch": "mixed"}
+            "chunked_prefill": "prefill", "mixed_batch": "mixed", "batched_decode_sym": "decode"}
 KERNEL_OF_ENTRY = {"decode": "split_attn_kernel", "verify": "split_attn_kernel",
                    "prefill": "prefill_attn_kernel",
                    "mixed": "split_attn_kernel + prefill_attn_kernel"}
@@ -120,8 +121,9 @@ def algorithmic_work(inp, q_lo=1, q_hi=None):
         vis = int((p - lo + 1).sum())
         qctx += vis
         pairs += vis * inp.num_q_heads
-    kv_bytes = keys * inp.num_kv_heads * (192 + 128) * esize
-    return {"kv_bytes": kv_bytes, "pairs": pairs, "flops": 640 * pairs, "q_ctx": qctx}
+    dqk, dv = inp.q.shape[2], inp.v_cache.shape[3]
+    kv_bytes = keys * inp.num_kv_heads * (dqk + dv) * esize
+    return {"kv_bytes": kv_bytes, "pairs": pairs, "flops": 2 * (dqk + dv) * pairs, "q_ctx": qctx}
 
 
 _CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/|\s+', re.S)
@@ -265,7 +267,7 @@ def measure_kv_write(name, steps, warmup, events, target_bytes=1 << 30):
              for (kn, vn), (kc, vc) in zip(news, caches)]
     total_ms, wall, kern = time_calls(calls, steps, warmup, events, stream)
     esize = 1 if inp.kv_dtype == "fp8" else 2
-    nbytes = T * H * (192 + 128) * (2 + esize)
+    nbytes = T * H * (inp.q.shape[2] + inp.v_cache.shape[3]) * (2 + esize)
     ms = sum(kern) / len(kern)
     achieved = nbytes / (ms * 1e-3) / 1e9
     step_ms = total_ms / steps
@@ -318,7 +320,8 @@ def measure_context_split(steps, warmup, events, parts=2, target_bytes=1 << 30):
     comb = [B.prepared_combine(parts, rows, inp.num_q_heads, out_parts, lse_parts, dev.sinks, out,
                                None, stream)]
     c_total, _, c_kern = time_calls(comb, steps, warmup, events, stream)
-    kv_bytes = int(hi.astype(np.int64).sum() - lo.sum()) * inp.num_kv_heads * (192 + 128) * 2
+    kv_bytes = (int(hi.astype(np.int64).sum() - lo.sum()) * inp.num_kv_heads
+                * (inp.q.shape[2] + inp.v_cache.shape[3]) * 2)
     ms = sum(kern) / len(kern)
     achieved = kv_bytes / (ms * 1e-3) / 1e9
     return {"entry": "partial+combine", "workload": "batched_decode", "parts": parts,
@@ -461,8 +464,10 @@ def cpu_baseline(name, seconds):
                 paged_attention(**args, tokens=toks)
                 p = L - n + (toks - starts[b])
                 lo = np.maximum(0, p - inp.window + 1) if inp.window > 0 else np.zeros_like(p)
-                done_bytes += int(p.max() + 1 - lo.min()) * inp.num_kv_heads * 320 * esize
-                done_flops += 640 * int((p - lo + 1).sum()) * inp.num_q_heads
+                done_bytes += (int(p.max() + 1 - lo.min()) * inp.num_kv_heads
+                               * (inp.q.shape[2] + inp.v_cache.shape[3]) * esize)
+                done_flops += (2 * (inp.q.shape[2] + inp.v_cache.shape[3]) * int((p - lo + 1).sum())
+                               * inp.num_q_heads)
                 n_tok += len(toks)
                 if time.perf_counter() - t0 >= seconds:
                     break
@@ -535,7 +540,7 @@ def main():
     if not args.no_extra:
         extra = {}
         for other in ("verify_long", "swa_sinks_fp8_p1", "swa_sinks_fp8_p128", "chunked_prefill",
-                      "mixed_batch"):
+                      "mixed_batch", "batched_decode_sym"):
             if other == name:
                 continue
             print(f"[bench] {other}: generating and measuring", file=sys.stderr, flush=True)

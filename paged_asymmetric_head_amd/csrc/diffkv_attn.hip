@@ -37,7 +37,8 @@ int validate_desc(const diffkv_attn_desc* d, int entry) {
   if (entry < DIFFKV_ENTRY_DECODE || entry > DIFFKV_ENTRY_MIXED) return DIFFKV_INVALID_ARGUMENT;
   if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1) return DIFFKV_INVALID_ARGUMENT;
   if (d->num_q_heads % d->num_kv_heads != 0) return DIFFKV_INVALID_ARGUMENT;
-  if (d->head_dim_qk != kHeadDimQK || d->head_dim_v != kHeadDimV) return DIFFKV_UNSUPPORTED;
+  if ((d->head_dim_qk != kHeadDimQK && d->head_dim_qk != kHeadDimQKSym) || d->head_dim_v != kHeadDimV)
+    return DIFFKV_UNSUPPORTED;
   if (!is_pow2(d->page_size) || d->page_size > 256) return DIFFKV_UNSUPPORTED;
   if (d->kv_dtype != DIFFKV_KV_BF16 && d->kv_dtype != DIFFKV_KV_FP8_E4M3) return DIFFKV_UNSUPPORTED;
   if (d->num_pages < 1 || d->max_seq_len < 1 || d->max_q_len < 1 || d->total_q < 1)
@@ -70,39 +71,47 @@ hipError_t launch_main(const void* fn, dim3 grid, dim3 block, void** args, hipSt
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
-template <bool FP8, int RT, bool DIRECT, bool COUNT, bool UPAGE>
+template <bool FP8, int RT, bool DIRECT, bool COUNT, bool UPAGE, int DQK>
 hipError_t launch_split_kernel(const SplitArgs& a, dim3 grid, hipStream_t stream) {
   void* args[] = {const_cast<SplitArgs*>(&a)};
   constexpr int NS = kSplitStages<FP8>;
   return launch_main(
-      reinterpret_cast<const void*>(&split_attn_kernel<FP8, RT, DIRECT, COUNT, UPAGE, NS>), grid,
-      dim3(256), args, stream);
+      reinterpret_cast<const void*>(&split_attn_kernel<FP8, RT, DIRECT, COUNT, UPAGE, NS, DQK>),
+      grid, dim3(256), args, stream);
 }
 
-template <bool FP8, int RT, bool UPAGE>
+template <bool FP8, int RT, bool UPAGE, int DQK>
 hipError_t dispatch_split_rt(const SplitArgs& a, dim3 grid, bool direct, bool count, hipStream_t st) {
-  if (direct) return count ? launch_split_kernel<FP8, RT, true, true, UPAGE>(a, grid, st)
-                           : launch_split_kernel<FP8, RT, true, false, UPAGE>(a, grid, st);
-  return count ? launch_split_kernel<FP8, RT, false, true, UPAGE>(a, grid, st)
-               : launch_split_kernel<FP8, RT, false, false, UPAGE>(a, grid, st);
+  if (direct) return count ? launch_split_kernel<FP8, RT, true, true, UPAGE, DQK>(a, grid, st)
+                           : launch_split_kernel<FP8, RT, true, false, UPAGE, DQK>(a, grid, st);
+  return count ? launch_split_kernel<FP8, RT, false, true, UPAGE, DQK>(a, grid, st)
+               : launch_split_kernel<FP8, RT, false, false, UPAGE, DQK>(a, grid, st);
 }
 
 // UPAGE: pages of at least one 64-key tile, so a tile never straddles pages.
-template <bool FP8>
-hipError_t dispatch_split(const SplitArgs& a, int rt, bool upage, dim3 grid, bool direct,
-                          bool count, hipStream_t st) {
+template <bool FP8, int DQK>
+hipError_t dispatch_split_dqk(const SplitArgs& a, int rt, bool upage, dim3 grid, bool direct,
+                              bool count, hipStream_t st) {
   if (upage) {
     switch (rt) {
-      case 1: return dispatch_split_rt<FP8, 1, true>(a, grid, direct, count, st);
-      case 2: return dispatch_split_rt<FP8, 2, true>(a, grid, direct, count, st);
-      default: return dispatch_split_rt<FP8, 4, true>(a, grid, direct, count, st);
+      case 1: return dispatch_split_rt<FP8, 1, true, DQK>(a, grid, direct, count, st);
+      case 2: return dispatch_split_rt<FP8, 2, true, DQK>(a, grid, direct, count, st);
+      default: return dispatch_split_rt<FP8, 4, true, DQK>(a, grid, direct, count, st);
     }
   }
   switch (rt) {
-    case 1: return dispatch_split_rt<FP8, 1, false>(a, grid, direct, count, st);
-    case 2: return dispatch_split_rt<FP8, 2, false>(a, grid, direct, count, st);
-    default: return dispatch_split_rt<FP8, 4, false>(a, grid, direct, count, st);
+    case 1: return dispatch_split_rt<FP8, 1, false, DQK>(a, grid, direct, count, st);
+    case 2: return dispatch_split_rt<FP8, 2, false, DQK>(a, grid, direct, count, st);
+    default: return dispatch_split_rt<FP8, 4, false, DQK>(a, grid, direct, count, st);
   }
+}
+
+template <bool FP8>
+hipError_t dispatch_split(const SplitArgs& a, int dqk, int rt, bool upage, dim3 grid, bool direct,
+                          bool count, hipStream_t st) {
+  return dqk == kHeadDimQKSym
+             ? dispatch_split_dqk<FP8, kHeadDimQKSym>(a, rt, upage, grid, direct, count, st)
+             : dispatch_split_dqk<FP8, kHeadDimQK>(a, rt, upage, grid, direct, count, st);
 }
 
 // Merge shape by the bound on chunks per pair: one wave with 16 loads when
@@ -125,19 +134,27 @@ hipError_t launch_merge(const SplitArgs& a, int rows, int max_chunks, dim3 grid,
   return hipLaunchKernel(fn, grid, dim3(threads), args, 0, stream);
 }
 
-template <bool FP8, bool UPAGE, bool COUNT>
+template <bool FP8, bool UPAGE, bool COUNT, int DQK>
 hipError_t launch_prefill_kernel(const SplitArgs& a, dim3 grid, hipStream_t stream) {
   void* args[] = {const_cast<SplitArgs*>(&a)};
-  return launch_main(reinterpret_cast<const void*>(&prefill_attn_kernel<FP8, UPAGE, COUNT>), grid,
-                     dim3(kPfThreads), args, stream);
+  return launch_main(reinterpret_cast<const void*>(&prefill_attn_kernel<FP8, UPAGE, COUNT, DQK>),
+                     grid, dim3(kPfThreads), args, stream);
+}
+
+template <bool FP8, int DQK>
+hipError_t dispatch_prefill_dqk(const SplitArgs& a, bool upage, bool count, dim3 grid,
+                                hipStream_t st) {
+  if (upage) return count ? launch_prefill_kernel<FP8, true, true, DQK>(a, grid, st)
+                          : launch_prefill_kernel<FP8, true, false, DQK>(a, grid, st);
+  return count ? launch_prefill_kernel<FP8, false, true, DQK>(a, grid, st)
+               : launch_prefill_kernel<FP8, false, false, DQK>(a, grid, st);
 }
 
 template <bool FP8>
-hipError_t dispatch_prefill(const SplitArgs& a, bool upage, bool count, dim3 grid, hipStream_t st) {
-  if (upage) return count ? launch_prefill_kernel<FP8, true, true>(a, grid, st)
-                          : launch_prefill_kernel<FP8, true, false>(a, grid, st);
-  return count ? launch_prefill_kernel<FP8, false, true>(a, grid, st)
-               : launch_prefill_kernel<FP8, false, false>(a, grid, st);
+hipError_t dispatch_prefill(const SplitArgs& a, int dqk, bool upage, bool count, dim3 grid,
+                            hipStream_t st) {
+  return dqk == kHeadDimQKSym ? dispatch_prefill_dqk<FP8, kHeadDimQKSym>(a, upage, count, grid, st)
+                              : dispatch_prefill_dqk<FP8, kHeadDimQK>(a, upage, count, grid, st);
 }
 
 hipError_t launch_fill(int32_t* p, size_t n, hipStream_t stream) {
@@ -230,8 +247,10 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
     if (entry == DIFFKV_ENTRY_MIXED) sa.q_hi = kMixedSplitMaxQ;
     const dim3 grid((unsigned)plan.grid_x, d->num_kv_heads);
     hipError_t e =
-        fp8 ? dispatch_split<true>(sa, plan.row_tiles, upage, grid, plan.direct, count, stream)
-            : dispatch_split<false>(sa, plan.row_tiles, upage, grid, plan.direct, count, stream);
+        fp8 ? dispatch_split<true>(sa, d->head_dim_qk, plan.row_tiles, upage, grid, plan.direct, count,
+                                   stream)
+            : dispatch_split<false>(sa, d->head_dim_qk, plan.row_tiles, upage, grid, plan.direct, count,
+                                    stream);
     if (e == hipSuccess && !plan.direct)
       e = launch_merge(sa, plan.rows, plan.max_chunks,
                        dim3(sd.max_q_len * G, d->batch * d->num_kv_heads), stream);
@@ -247,8 +266,8 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
     pa.n_qtiles = prefill_row_blocks(*d);
     if (entry == DIFFKV_ENTRY_MIXED) pa.q_lo = kMixedSplitMaxQ + 1;
     const dim3 grid(pa.n_qtiles, d->batch * d->num_kv_heads);
-    const hipError_t e = fp8 ? dispatch_prefill<true>(pa, upage, count, grid, stream)
-                             : dispatch_prefill<false>(pa, upage, count, grid, stream);
+    const hipError_t e = fp8 ? dispatch_prefill<true>(pa, d->head_dim_qk, upage, count, grid, stream)
+                             : dispatch_prefill<false>(pa, d->head_dim_qk, upage, count, grid, stream);
     if (e != hipSuccess) return DIFFKV_HIP_ERROR;
   }
   return DIFFKV_OK;
@@ -281,10 +300,13 @@ int run_kv_write(const diffkv_attn_desc* d, const void* k_new, const void* v_new
   a.k_scale = fp8 ? k_scale : 1.f;
   a.v_scale = fp8 ? v_scale : 1.f;
   void* args[] = {&a};
-  const long long units = (long long)d->max_q_len * d->num_kv_heads * (kKUnits + kVUnits);
+  const long long units = (long long)d->max_q_len * d->num_kv_heads * (d->head_dim_qk / 8 + kVUnits);
   const dim3 grid((unsigned)((units + 255) / 256), d->batch);
-  const void* fn = fp8 ? reinterpret_cast<const void*>(&kv_write_kernel<true>)
-                       : reinterpret_cast<const void*>(&kv_write_kernel<false>);
+  const bool sym = d->head_dim_qk == kHeadDimQKSym;
+  const void* fn = fp8 ? (sym ? reinterpret_cast<const void*>(&kv_write_kernel<true, kHeadDimQKSym>)
+                              : reinterpret_cast<const void*>(&kv_write_kernel<true, kHeadDimQK>))
+                       : (sym ? reinterpret_cast<const void*>(&kv_write_kernel<false, kHeadDimQKSym>)
+                              : reinterpret_cast<const void*>(&kv_write_kernel<false, kHeadDimQK>));
   return launch_main(fn, grid, dim3(256), args, stream) == hipSuccess ? DIFFKV_OK
                                                                        : DIFFKV_HIP_ERROR;
 }

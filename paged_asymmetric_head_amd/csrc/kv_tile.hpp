@@ -16,20 +16,22 @@
 
 namespace diffkv {
 
-constexpr int kKLdsStride = kHeadDimQK + 8;   // bf16 per K row in LDS (400 B, conflict-free reads)
+// bf16 per K row in LDS: the row plus 16 bytes (400 B at QK 192, 272 B at
+// 128), so the 16 rows a K-fragment read touches fall in distinct banks.
+template <int DQK> constexpr int kKLdsStride = DQK + 8;
 constexpr int kVLdsStride = kHeadDimV + 16;   // bf16 per V row in LDS (288 B: the 16 rows of
                                                // a transposing read fall in distinct bank windows)
-constexpr int kKLdsElems = kTileKeys * kKLdsStride;
+template <int DQK> constexpr int kKLdsElems = kTileKeys * kKLdsStride<DQK>;
 constexpr int kVLdsElems = kTileKeys * kVLdsStride;
 
 // Sixteen zero bytes (static device memory is zero-filled at load): the
 // source of every load whose key lies outside the range a tile may read.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[16];
 
-template <bool FP8, bool UPAGE, int NT = 256>
+template <bool FP8, bool UPAGE, int DQK, int NT = 256>
 struct KvTile {
   static constexpr int ESZ = FP8 ? 1 : 2;
-  static constexpr int K_UPR = kHeadDimQK * ESZ / 16;   // 16-byte units per K row
+  static constexpr int K_UPR = DQK * ESZ / 16;          // 16-byte units per K row
   static constexpr int V_UPR = kHeadDimV * ESZ / 16;
   static constexpr int K_UNITS = kTileKeys * K_UPR;     // units per tile
   static constexpr int V_UNITS = kTileKeys * V_UPR;
@@ -58,10 +60,10 @@ struct KvTile {
   __device__ __forceinline__ KvTile(const uint8_t* k_cache, const uint8_t* v_cache,
                                     const int32_t* bt_row, int hkv, int g, int log2_page,
                                     int lo, int hi, int t_end, int thread)
-      : k_head(k_cache + (size_t)g * kHeadDimQK * ESZ),
+      : k_head(k_cache + (size_t)g * DQK * ESZ),
         v_head(v_cache + (size_t)g * kHeadDimV * ESZ),
         bt(bt_row),
-        k_slot_bytes((size_t)hkv * kHeadDimQK * ESZ),
+        k_slot_bytes((size_t)hkv * DQK * ESZ),
         v_slot_bytes((size_t)hkv * kHeadDimV * ESZ),
         lp(log2_page), pmask((1 << log2_page) - 1), kv_lo(lo), kv_hi(hi), t_last(t_end - 1),
         tid(thread) {
@@ -148,11 +150,11 @@ struct KvTile {
       if constexpr (FP8) {
         const u32x2 c0 = e4m3x4_to_bf16x4(st.k[k].x), c1 = e4m3x4_to_bf16x4(st.k[k].y);
         const u32x2 c2 = e4m3x4_to_bf16x4(st.k[k].z), c3 = e4m3x4_to_bf16x4(st.k[k].w);
-        u32x4* dst = reinterpret_cast<u32x4*>(k_lds + row * kKLdsStride + piece * 16);
+        u32x4* dst = reinterpret_cast<u32x4*>(k_lds + row * kKLdsStride<DQK> + piece * 16);
         dst[0] = u32x4{c0.x, c0.y, c1.x, c1.y};
         dst[1] = u32x4{c2.x, c2.y, c3.x, c3.y};
       } else {
-        *reinterpret_cast<u32x4*>(k_lds + row * kKLdsStride + piece * 8) = st.k[k];
+        *reinterpret_cast<u32x4*>(k_lds + row * kKLdsStride<DQK> + piece * 8) = st.k[k];
       }
     }
 #pragma unroll

@@ -2,14 +2,15 @@
 //
 // The FP8 KV cache of "diffbot/MiMo-V2.6-Flash-RL-FP8KV-W4A8-2x-RTX-PRO-6000"
 // (intro: E4M3 K/V with per-tensor scales) is filled one step before
-// attention reads it; K (192 wide) and V (128 wide) live in two caches
+// attention reads it; K (192 wide, or 128 for symmetric heads) and V (128
+// wide) live in two caches
 // ("sglang PR 32818, Route asymmetric-KV models to fa4 on SM100").  New token
 // i of sequence b sits at position p = L - n + i and goes to slot p % P of
 // page block_table[b][p / P].  bf16 caches take the rows as they are; FP8
 // caches take E4M3FN codes of x / scale (division in fp32, clamped to +-448,
 // round to nearest even, NaN kept with its sign).
 //
-// A row is cut into 8-value units (K 24, V 16 per KV head); one thread per
+// A row is cut into 8-value units (K 24 or 16, V 16 per KV head); one thread per
 // unit, the units of one sequence's new tokens numbered token-major over a
 // grid of (ceil(max_q_len * units per token / 256), batch) workgroups, so
 // consecutive threads read and write contiguous runs of each row.  A
@@ -23,9 +24,9 @@
 namespace diffkv {
 
 struct KvWriteArgs {
-  const uint16_t* k_new;     // bf16 [total_q, Hkv, 192]
+  const uint16_t* k_new;     // bf16 [total_q, Hkv, DQK]
   const uint16_t* v_new;     // bf16 [total_q, Hkv, 128]
-  uint8_t* k_cache;          // [pages, P, Hkv, 192] bf16 or E4M3 codes
+  uint8_t* k_cache;          // [pages, P, Hkv, DQK] bf16 or E4M3 codes
   uint8_t* v_cache;          // [pages, P, Hkv, 128]
   const int32_t* block_table;
   const int32_t* seq_lens;
@@ -34,8 +35,7 @@ struct KvWriteArgs {
   float k_scale, v_scale;    // FP8 only
 };
 
-constexpr int kKUnits = kHeadDimQK / 8;     // 8-value units per K row
-constexpr int kVUnits = kHeadDimV / 8;
+constexpr int kVUnits = kHeadDimV / 8;      // 8-value units per V row
 
 // Eight fp32 values -> eight E4M3FN codes (byte j = value j): clamp to
 // +-448 (NaN kept), v_cvt_pk_fp8_f32 rounds to nearest even; NaN lanes get
@@ -62,8 +62,9 @@ __device__ __forceinline__ u32x2 encode8_e4m3(const float (&y)[8]) {
   return u32x2{w[0], w[1]};
 }
 
-template <bool FP8>
+template <bool FP8, int DQK>
 __global__ __launch_bounds__(256) void kv_write_kernel(const KvWriteArgs a) {
+  constexpr int kKUnits = DQK / 8;          // 8-value units per K row
   const int b = blockIdx.y;
   const int n = a.q_lens ? a.q_lens[b] : 1;
   const int per_token = a.hkv * (kKUnits + kVUnits);
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const KvWriteArgs a) {
   const int c = rem - g * (kKUnits + kVUnits);
   const bool is_k = c < kKUnits;
   const int piece = is_k ? c : c - kKUnits;
-  const int width = is_k ? kHeadDimQK : kHeadDimV;
+  const int width = is_k ? DQK : kHeadDimV;
   const int p = a.seq_lens[b] - n + i;
   if (p < 0 || (p >> a.log2_page) >= a.bt_stride || r0 + i >= a.total_q) return;
   const int page = a.block_table[(size_t)b * a.bt_stride + (p >> a.log2_page)];

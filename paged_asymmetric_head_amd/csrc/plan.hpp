@@ -13,7 +13,8 @@
 
 namespace diffkv {
 
-constexpr int kHeadDimQK = 192;
+constexpr int kHeadDimQK = 192;      // key head dim of the asymmetric layers
+constexpr int kHeadDimQKSym = 128;   // key head dim of symmetric (128/128) heads
 constexpr int kHeadDimV = 128;
 constexpr int kTileKeys = 64;        // keys per split-kernel tile
 constexpr int kTargetCUs = 256;      // MI355X: 256 compute units in 8 XCDs

@@ -45,13 +45,14 @@ constexpr int kPfThreads = 64 * kPfWaves;
 #define DIFFKV_PREFILL_STAGES_BF16 1
 #endif
 
-template <bool FP8, bool UPAGE, bool COUNT>
+template <bool FP8, bool UPAGE, bool COUNT, int DQK>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_attn_kernel(const SplitArgs a) {
-  using IO = KvTile<FP8, UPAGE, kPfThreads>;
+  constexpr int QC = DQK / 32;               // 32-dim contraction steps of QK^T
+  using IO = KvTile<FP8, UPAGE, DQK, kPfThreads>;
   constexpr int NS = FP8 ? DIFFKV_PREFILL_STAGES_FP8 : DIFFKV_PREFILL_STAGES_BF16;
   constexpr int RT = kPfRowTiles;
-  constexpr int LDS_TILE = kKLdsElems + kVLdsElems;
+  constexpr int LDS_TILE = kKLdsElems<DQK> + kVLdsElems;
 
   // Two LDS tiles: the next tile is widened into one while the matrix cores
   // read the other, one barrier per tile.
@@ -100,7 +101,7 @@ void prefill_attn_kernel(const SplitArgs a) {
   // This lane's query row in each of the wave's row tiles.
   bool row_ok[RT];
   int tok[RT], hh[RT], lo_row[RT], hi_row[RT];
-  u32x4 qreg[RT][6];
+  u32x4 qreg[RT][QC];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int R = r_first + (wave * RT + rt) * 16 + col;
@@ -110,9 +111,9 @@ void prefill_attn_kernel(const SplitArgs a) {
     const int p_row = L - n + tok[rt];
     lo_row[rt] = a.window > 0 ? max(0, p_row - a.window + 1) : 0;
     hi_row[rt] = row_ok[rt] ? p_row : -1;
-    const uint16_t* qp = a.q + ((size_t)(r0 + tok[rt]) * a.hq + hh[rt]) * kHeadDimQK + 8 * grp;
+    const uint16_t* qp = a.q + ((size_t)(r0 + tok[rt]) * a.hq + hh[rt]) * DQK + 8 * grp;
 #pragma unroll
-    for (int c = 0; c < 6; ++c)
+    for (int c = 0; c < QC; ++c)
       qreg[rt][c] = *reinterpret_cast<const u32x4*>(
           row_ok[rt] ? reinterpret_cast<const uint8_t*>(qp + 32 * c) : g_zero_row);
   }
@@ -121,7 +122,7 @@ void prefill_attn_kernel(const SplitArgs a) {
   // (t - t_begin) % NS.  Tile t_begin goes to LDS now.
   {
     uint16_t* first = lds + (t_begin & 1) * LDS_TILE;
-    io.store(st[0], first, first + kKLdsElems);
+    io.store(st[0], first, first + kKLdsElems<DQK>);
   }
   io.fetch_data(t_begin + NS, pg[0], st[0]);
   io.fetch_pages(t_begin + 2 * NS, pg[0]);
@@ -147,11 +148,11 @@ void prefill_attn_kernel(const SplitArgs a) {
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) sacc[rt][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 6; ++c)
+    for (int c = 0; c < QC; ++c)
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
         const u32x4 kf =
-            *reinterpret_cast<const u32x4*>(k_lds + (sub * 16 + col) * kKLdsStride + 8 * grp + 32 * c);
+            *reinterpret_cast<const u32x4*>(k_lds + (sub * 16 + col) * kKLdsStride<DQK> + 8 * grp + 32 * c);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) sacc[rt][sub] = mfma_16x16x32(kf, qreg[rt][c], sacc[rt][sub]);
       }
@@ -240,11 +241,11 @@ void prefill_attn_kernel(const SplitArgs a) {
       const int t = t0 + i;
       uint16_t* cur = lds + (t & 1) * LDS_TILE;
       uint16_t* nxt = lds + ((t + 1) & 1) * LDS_TILE;
-      if (t < t_end) compute_tile(t, cur, cur + kKLdsElems);
+      if (t < t_end) compute_tile(t, cur, cur + kKLdsElems<DQK>);
       // Widen tile t + 1 into the other buffer (its last readers passed the
       // barrier that ended the previous tile), then start loading t + 1 + NS.
       const int j = (i + 1) % NS;   // a constant once the loop is unrolled
-      io.store(st[j], nxt, nxt + kKLdsElems);
+      io.store(st[j], nxt, nxt + kKLdsElems<DQK>);
       io.fetch_data(t + 1 + NS, pg[j], st[j]);
       io.fetch_pages(t + 1 + 2 * NS, pg[j]);
       __syncthreads();

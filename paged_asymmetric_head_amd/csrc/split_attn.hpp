@@ -1,5 +1,6 @@
 // Split-KV paged attention for decode and speculative verify on gfx950, plus
-// the log-sum-exp merge of the split partials.
+// the log-sum-exp merge of the split partials.  K rows are DQK wide (192, or
+// 128 for symmetric heads), V rows 128.
 //
 // Work decomposition ("diffbot/MiMo-V2.6-Flash-RL-FP8KV-W4A8-2x-RTX-PRO-6000",
 // What the kernels do: without split-KV a multi-token verify ran on a handful
@@ -196,16 +197,17 @@ struct SplitPlanner {
   }
 };
 
-template <bool FP8, int RT, bool DIRECT, bool COUNT, bool UPAGE, int NS>
+template <bool FP8, int RT, bool DIRECT, bool COUNT, bool UPAGE, int NS, int DQK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSplitWavesPerEu, 8)))
 void split_attn_kernel(const SplitArgs a) {
   constexpr int ROWS = 16 * RT;
   constexpr int KW = 4 / RT;                 // waves splitting the keys of one row tile
   constexpr int SUBS = kTileKeys / 16 / KW;  // 16-key subtiles per wave per tile
-  using IO = KvTile<FP8, UPAGE>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kKLdsElems + kVLdsElems];
+  constexpr int QC = DQK / 32;               // 32-dim contraction steps of QK^T
+  using IO = KvTile<FP8, UPAGE, DQK>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kKLdsElems<DQK> + kVLdsElems];
   uint16_t* k_lds = lds;
-  uint16_t* v_lds = lds + kKLdsElems;
+  uint16_t* v_lds = lds + kKLdsElems<DQK>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -288,11 +290,11 @@ void split_attn_kernel(const SplitArgs a) {
   const int hi_row = row_ok ? min(p_row, khi - 1) : -1;   // empty interval for padding rows
 
   // Q^T operand: contraction chunk c carries dims 32c + 8*grp .. +7.
-  u32x4 qreg[6];
+  u32x4 qreg[QC];
   {
-    const uint16_t* qp = a.q + ((size_t)(r0 + tok) * a.hq + h) * kHeadDimQK + 8 * grp;
+    const uint16_t* qp = a.q + ((size_t)(r0 + tok) * a.hq + h) * DQK + 8 * grp;
 #pragma unroll
-    for (int c = 0; c < 6; ++c)
+    for (int c = 0; c < QC; ++c)
       qreg[c] = *reinterpret_cast<const u32x4*>(row_ok ? reinterpret_cast<const uint8_t*>(qp + 32 * c)
                                                        : g_zero_row);
   }
@@ -321,10 +323,10 @@ void split_attn_kernel(const SplitArgs a) {
 #pragma unroll
     for (int sub = 0; sub < SUBS; ++sub) sacc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 6; ++c)
+    for (int c = 0; c < QC; ++c)
 #pragma unroll
       for (int sub = 0; sub < SUBS; ++sub) {
-        const uint16_t* kp = k_lds + ((kg * SUBS + sub) * 16 + col) * kKLdsStride + 8 * grp + 32 * c;
+        const uint16_t* kp = k_lds + ((kg * SUBS + sub) * 16 + col) * kKLdsStride<DQK> + 8 * grp + 32 * c;
         sacc[sub] = mfma_16x16x32(*reinterpret_cast<const u32x4*>(kp), qreg[c], sacc[sub]);
       }
 
@@ -425,7 +427,7 @@ void split_attn_kernel(const SplitArgs a) {
   // Waves that split the keys of one row tile combine through LDS.
   if constexpr (KW > 1) {
     constexpr int STR = 34;
-    static_assert(4 * 64 * STR * 4 <= (kKLdsElems + kVLdsElems) * 2, "reduction fits");
+    static_assert(4 * 64 * STR * 4 <= (kKLdsElems<DQK> + kVLdsElems) * 2, "reduction fits");
     __syncthreads();
     float* red = reinterpret_cast<float*>(lds);
     float* mine = red + (wave * 64 + lane) * STR;

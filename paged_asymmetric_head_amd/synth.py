@@ -38,8 +38,8 @@ class PagedInputs:
     num_kv_heads: int
     page_size: int
     kv_dtype: str                 # "bf16" or "fp8"
-    q: np.ndarray                 # uint16 [total_q, Hq, 192] (bf16 codes)
-    k_cache: np.ndarray           # uint16|uint8 [pages, P, Hkv, 192]
+    q: np.ndarray                 # uint16 [total_q, Hq, Dqk] (bf16 codes), Dqk 192 or 128
+    k_cache: np.ndarray           # uint16|uint8 [pages, P, Hkv, Dqk]
     v_cache: np.ndarray           # uint16|uint8 [pages, P, Hkv, 128]
     block_table: np.ndarray       # int32 [B, stride]
     seq_lens: np.ndarray          # int32 [B]
@@ -52,7 +52,7 @@ class PagedInputs:
     max_seq_len: int              # host-side bound used to size the launch
     max_q_len: int
     written_start: np.ndarray     # int64 [B]: first position holding data
-    logical_k: list = field(default_factory=list)   # per seq: codes [L - start, Hkv, 192]
+    logical_k: list = field(default_factory=list)   # per seq: codes [L - start, Hkv, Dqk]
     logical_v: list = field(default_factory=list)   # per seq: codes [L - start, Hkv, 128]
 
     @property
@@ -102,13 +102,14 @@ def to_e4m3fn_codes(x, scale):
 def make_paged_inputs(seed, *, seq_lens, q_lens, num_q_heads, num_kv_heads, page_size,
                       kv_dtype="bf16", window=0, sinks=False, softmax_scale=None,
                       extra_pages=0, block_table_stride=None, write_align=None,
-                      max_seq_len=None, name="custom"):
+                      max_seq_len=None, head_dim_qk=HEAD_DIM_QK, name="custom"):
     """Build one workload.
 
     seq_lens   list of ints, or (lo, hi) for integers uniform in [lo, hi]
                together with batch taken from q_lens when that is a list, or
                a list mixing ints and (lo, hi) pairs (one draw per pair).
     q_lens     int (same for every sequence) or list.
+    head_dim_qk  key/query head dim (192, or 128 for symmetric heads); V is 128.
     write_align  with a window, positions before the start of the aligned
                block (of this many tokens) holding the window union's first
                key stay unwritten (NaN); otherwise every position is written.
@@ -141,7 +142,7 @@ def make_paged_inputs(seed, *, seq_lens, q_lens, num_q_heads, num_kv_heads, page
         max_seq_len = bound
     Hq, Hkv, P = int(num_q_heads), int(num_kv_heads), int(page_size)
     if softmax_scale is None:
-        softmax_scale = 1.0 / math.sqrt(HEAD_DIM_QK)
+        softmax_scale = 1.0 / math.sqrt(head_dim_qk)
 
     pages_per_seq = -(-L // P)
     num_pages = int(pages_per_seq.sum()) + int(extra_pages)
@@ -156,14 +157,14 @@ def make_paged_inputs(seed, *, seq_lens, q_lens, num_q_heads, num_kv_heads, page
         off += k
 
     total_q = int(n.sum())
-    q = to_bf16_bits(r_q.standard_normal((total_q, Hq, HEAD_DIM_QK), dtype=np.float32))
+    q = to_bf16_bits(r_q.standard_normal((total_q, Hq, head_dim_qk), dtype=np.float32))
 
     W = int(window)
     start = np.zeros(batch, dtype=np.int64)
     if W > 0 and write_align:
         first_key = np.maximum(0, L - n - W + 1)
         start = (first_key // int(write_align)) * int(write_align)
-    k_f = [r_k.standard_normal((int(L[b] - start[b]), Hkv, HEAD_DIM_QK), dtype=np.float32)
+    k_f = [r_k.standard_normal((int(L[b] - start[b]), Hkv, head_dim_qk), dtype=np.float32)
            for b in range(batch)]
     v_f = [r_v.standard_normal((int(L[b] - start[b]), Hkv, HEAD_DIM_V), dtype=np.float32)
            for b in range(batch)]
@@ -183,7 +184,7 @@ def make_paged_inputs(seed, *, seq_lens, q_lens, num_q_heads, num_kv_heads, page
     del k_f, v_f
 
     nan_code = np.iinfo(code_t).max          # 0xFFFF bf16 NaN, 0xFF E4M3FN NaN
-    k_cache = np.full((num_pages, P, Hkv, HEAD_DIM_QK), nan_code, dtype=code_t)
+    k_cache = np.full((num_pages, P, Hkv, head_dim_qk), nan_code, dtype=code_t)
     v_cache = np.full((num_pages, P, Hkv, HEAD_DIM_V), nan_code, dtype=code_t)
     for b in range(batch):
         pos = np.arange(start[b], L[b], dtype=np.int64)
@@ -228,6 +229,9 @@ WORKLOADS = {
     # One sequence: 4096 new tokens after 26624 cached, GQA 32/2, FP8 K/V.
     "chunked_prefill": dict(seed=5, seq_lens=[30720], q_lens=4096, num_q_heads=32,
                             num_kv_heads=2, page_size=128, kv_dtype="fp8"),
+    # Symmetric 128/128 heads at the batched-decode shape.
+    "batched_decode_sym": dict(seed=7, seq_lens=(8192, 9216), q_lens=[1] * 32, num_q_heads=8,
+                               num_kv_heads=1, page_size=128, kv_dtype="bf16", head_dim_qk=128),
     # One serving step mixing the three kinds of sequence at the prefill
     # chunk's head shape (GQA 32/2, page 128, FP8 K/V): the 4096-token chunk
     # at 26K context, 4 verify blocks of 8 at 40000..50000 tokens and 32

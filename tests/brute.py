@@ -44,7 +44,7 @@ def brute_force(inp):
     row = 0
     for b in range(inp.batch):
         L, n, start = int(inp.seq_lens[b]), int(inp.q_lens[b]), int(inp.written_start[b])
-        K = lib_decode(inp.logical_k[b], inp.kv_dtype) * ks      # [L - start, Hkv, 192]
+        K = lib_decode(inp.logical_k[b], inp.kv_dtype) * ks      # [L - start, Hkv, Dqk]
         V = lib_decode(inp.logical_v[b], inp.kv_dtype) * vs
         vis = visible_matrix(L, n, inp.window)
         for i in range(n):

@@ -57,11 +57,14 @@ def test_validate_accepts_good_descriptors(lib):
     assert B.diffkv_attn_validate(good_desc(kv_dtype=B.KV_FP8_E4M3, page_size=1,
                                             block_table_stride=50000), B.ENTRY_VERIFY) == B.OK
     assert B.diffkv_attn_validate(good_desc(max_q_len=4096, total_q=4200), B.ENTRY_MIXED) == B.OK
+    for entry in (B.ENTRY_VERIFY, B.ENTRY_PREFILL, B.ENTRY_MIXED):     # symmetric 128/128 heads
+        assert B.diffkv_attn_validate(good_desc(head_dim_qk=128), entry) == B.OK
 
 
 @pytest.mark.parametrize("field,value,entry,status", [
     ("num_q_heads", 7, B.ENTRY_VERIFY, B.INVALID_ARGUMENT),       # Hq % Hkv with Hkv=2 below
-    ("head_dim_qk", 128, B.ENTRY_VERIFY, B.UNSUPPORTED),
+    ("head_dim_qk", 64, B.ENTRY_VERIFY, B.UNSUPPORTED),
+    ("head_dim_qk", 256, B.ENTRY_VERIFY, B.UNSUPPORTED),
     ("head_dim_v", 192, B.ENTRY_VERIFY, B.UNSUPPORTED),
     ("page_size", 96, B.ENTRY_VERIFY, B.UNSUPPORTED),
     ("page_size", 512, B.ENTRY_VERIFY, B.UNSUPPORTED),

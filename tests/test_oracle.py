@@ -84,6 +84,20 @@ def test_oracle_matches_brute_force(case):
     np.testing.assert_allclose(res.lse, bl, rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("kv,W,sinks", [("bf16", 0, True), ("fp8", 6, False)])
+def test_oracle_symmetric_heads_match_brute_force(kv, W, sinks):
+    """Symmetric 128/128 heads: the same definition with K as wide as V."""
+    inp = make_paged_inputs(150 + W, seq_lens=[30, 17], q_lens=[4, 2], num_q_heads=4,
+                            num_kv_heads=2, page_size=4, kv_dtype=kv, window=W, sinks=sinks,
+                            extra_pages=2, write_align=4 if W > 0 else None, head_dim_qk=128)
+    assert inp.q.shape[2] == 128 and inp.k_cache.shape[3] == 128
+    res = run(inp)
+    bo, bl, bc = brute_force(inp)
+    assert np.array_equal(res.count, bc)
+    np.testing.assert_allclose(res.out, bo, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(res.lse, bl, rtol=1e-12, atol=1e-13)
+
+
 def test_oracle_row_subset_matches_full():
     inp = make_paged_inputs(7, seq_lens=[40, 55, 23], q_lens=[3, 6, 2], num_q_heads=8,
                             num_kv_heads=2, page_size=4, kv_dtype="bf16", window=11, sinks=True)
