@@ -12,7 +12,10 @@
  *     prefill chunks at 26K context with 16 query heads per KV head, FP8
  *     E4M3 K/V converted as it is loaded.
  *   - "sglang PR 32818, Route asymmetric-KV models to fa4 on SM100": K and V
- *     rows have different widths, so they live in two separate caches.
+ *     rows have different widths, so they live in two separate caches; a
+ *     model's layer types may carry their own head-dim pairs (the change's
+ *     asymmetric-KV property), so the QK width D_qk is 192 or, for
+ *     symmetric heads, 128 (V stays 128).
  *
  * For sequence b with L = seq_lens[b] and n = q_lens[b], new token i (packed
  * row r0 + i, r0 = q_lens[0] + ... + q_lens[b-1]) sits at position
@@ -69,7 +72,7 @@ typedef struct diffkv_attn_desc {
   int32_t batch;               /* number of sequences B >= 1                        */
   int32_t num_q_heads;         /* Hq >= 1                                           */
   int32_t num_kv_heads;        /* Hkv >= 1, Hq % Hkv == 0, G = Hq / Hkv             */
-  int32_t head_dim_qk;         /* must be 192                                       */
+  int32_t head_dim_qk;         /* D_qk: 192, or 128 for symmetric 128/128 heads     */
   int32_t head_dim_v;          /* must be 128                                       */
   int32_t page_size;           /* P: a power of two in [1, 256]                     */
   int32_t num_pages;           /* pages in each cache                               */
@@ -85,8 +88,8 @@ typedef struct diffkv_attn_desc {
 
 /*
  * Attention over the paged cache.  Layouts (all row-major, contiguous):
- *   q            bf16  [total_q, Hq, 192]; sequence b's rows start at r0
- *   k_cache      bf16 or E4M3 [num_pages, P, Hkv, 192]
+ *   q            bf16  [total_q, Hq, D_qk]; sequence b's rows start at r0
+ *   k_cache      bf16 or E4M3 [num_pages, P, Hkv, D_qk]
  *   v_cache      bf16 or E4M3 [num_pages, P, Hkv, 128]
  *   block_table  int32 [batch, block_table_stride]; entry t is the physical
  *                page of the sequence's tokens [t*P, (t+1)*P).  Only entries
@@ -220,7 +223,7 @@ int diffkv_attn_combine(int32_t num_parts, int32_t rows, int32_t num_q_heads,
  * W4A8-2x-RTX-PRO-6000", intro: an E4M3 KV cache with per-tensor scales;
  * "sglang PR 32818": K and V in two caches of different row widths).
  *
- *   k_new        bf16 [total_q, Hkv, 192], packed by sequence like q above
+ *   k_new        bf16 [total_q, Hkv, D_qk], packed by sequence like q above
  *   v_new        bf16 [total_q, Hkv, 128]
  *   k_cache, v_cache, block_table, seq_lens, q_lens: as for attention (the
  *                same descriptor serves both calls; num_q_heads is checked
