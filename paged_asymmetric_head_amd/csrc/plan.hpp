@@ -67,8 +67,15 @@ inline long long max_keys_bound(const diffkv_attn_desc& d, int window) {
 #ifndef DIFFKV_SPLIT_WAVES_PER_EU
 #define DIFFKV_SPLIT_WAVES_PER_EU 2
 #endif
+#ifndef DIFFKV_SPLIT_SLOTS_PER_CU
+#define DIFFKV_SPLIT_SLOTS_PER_CU DIFFKV_SPLIT_WAVES_PER_EU
+#endif
+#ifndef DIFFKV_MIN_TILES_PER_SPLIT
+#define DIFFKV_MIN_TILES_PER_SPLIT 4
+#endif
 template <bool FP8> constexpr int kSplitStages = FP8 ? DIFFKV_FP8_STAGES : DIFFKV_BF16_STAGES;
 constexpr int kSplitWavesPerEu = DIFFKV_SPLIT_WAVES_PER_EU;
+constexpr int kSplitSlotsPerCu = DIFFKV_SPLIT_SLOTS_PER_CU;
 
 // Split plan from host bounds.  The kernels cut the keys on the device
 // (balanced chunks of C = max(kMinTilesPerSplit, ceil(T / slots)) tiles, T
@@ -80,9 +87,10 @@ constexpr int kSplitWavesPerEu = DIFFKV_SPLIT_WAVES_PER_EU;
 // kMinTilesPerSplit tiles (short windows).  A larger wgs_per_cu only grows
 // the bounds, so the workspace sized for 4 workgroups per CU covers every
 // launch.
-constexpr int kMinTilesPerSplit = 4;
+constexpr int kMinTilesPerSplit = DIFFKV_MIN_TILES_PER_SPLIT;
 
-inline SplitPlan plan_split(const diffkv_attn_desc& d, int window, int wgs_per_cu = 4) {
+inline SplitPlan plan_split(const diffkv_attn_desc& d, int window,
+                            int wgs_per_cu = kSplitSlotsPerCu > 4 ? kSplitSlotsPerCu : 4) {
   SplitPlan p;
   const int G = d.num_q_heads / d.num_kv_heads;
   const long long rows_pair = (long long)d.max_q_len * G;
