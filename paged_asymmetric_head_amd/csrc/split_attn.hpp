@@ -551,16 +551,21 @@ __global__ __launch_bounds__(64 * W) void split_merge_kernel(const SplitArgs a) 
   const int bg = blockIdx.y;
   const int b = bg / a.hkv, g = bg % a.hkv;
   const int G = a.group;
+  // The sequence's length, its pair's chunk range and its packed row start
+  // are independent loads: all go out before any is tested, so the partials
+  // are one memory round trip away.  The pair entry is read even for rows
+  // past the sequence's own (in bounds: every pair of the launch has one);
+  // those rows return before using it.
   const int n = a.q_lens ? a.q_lens[b] : 1;
-  if (n < a.q_lo || n > a.q_hi || R >= n * G) return;   // uniform over the workgroup
   const i32x2 pc = a.pair_chunks[(size_t)b * a.n_qtiles + qt];
+  const int r0 = seq_row_start(a.q_lens, b);
+  if (n < a.q_lo || n > a.q_hi || R >= n * G) return;   // uniform over the workgroup
   const int base = pc.x, S = pc.y;
   if (S <= 1) return;                       // written by the split kernel itself
   if (base < 0 || base + S > a.chunk_bound) return;
   // Waves in use: one when its K loads cover every chunk of the pair.
   const int nw = S <= K ? 1 : W;
   if (wave >= nw) return;
-  const int r0 = seq_row_start(a.q_lens, b);
 
   // Chunk j's partial row: chunk ids are consecutive within the pair.
   const size_t prow0 = ((size_t)base * a.hkv + g) * ROWS + r;
