@@ -147,134 +147,63 @@ void prefill_attn_kernel(const SplitArgs a) {
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) sacc[rt][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 pt[RT][2];
-    float alpha[RT];
-
-    // Scores of 16-key subtile sub for both row tiles (each K fragment read
-    // from LDS feeds both).  sacc[rt][sub][i] = raw score of key
-    // t*64 + sub*16 + 4*grp + i for this lane's row of row tile rt.
-    auto qk_subtile = [&](int sub) {
 #pragma unroll
-      for (int c = 0; c < QC; ++c) {
+    for (int c = 0; c < QC; ++c)
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
         const u32x4 kf =
             *reinterpret_cast<const u32x4*>(k_lds + (sub * 16 + col) * kKLdsStride<DQK> + 8 * grp + 32 * c);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) sacc[rt][sub] = mfma_16x16x32(kf, qreg[rt][c], sacc[rt][sub]);
       }
-    };
-    // P of subtile sub against the reference m_use (bf16, two words).
-    auto p_subtile = [&](int rt, int sub, float m_use) {
-      float pr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(__builtin_fmaf(sacc[rt][sub][i], scale, -m_use));
-      return u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
-    };
-    // One online-softmax update from the whole tile's scores (new reference,
-    // P, O rescale).
-    auto softmax_tile = [&]() {
-      u32x2 pb[RT][4];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[rt][sub][i]);
-        mx = max_over_lane_groups(mx);
-        const float m_new = next_reference(m[rt], mx * scale);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        alpha[rt] = fast_exp2(m[rt] - m_use);
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub) pb[rt][sub] = p_subtile(rt, sub, m_use);
-        pt[rt][0] = cat(pb[rt][0], pb[rt][1]);
-        pt[rt][1] = cat(pb[rt][2], pb[rt][3]);
-        m[rt] = m_new;
-        if (__ballot(alpha[rt] != 1.f)) {
-#pragma unroll
-          for (int nn = 0; nn < 8; ++nn) o[rt][nn] *= alpha[rt];
-        }
-      }
-    };
 
-    // Tiles every row sees whole skip the mask.  There each subtile's P is
-    // taken against the row's current reference while the next subtile's
-    // products run on the matrix cores (independent instructions the wave
-    // issues beside them); the tile's max decides afterwards whether that
-    // reference stands (the usual case: the max stays within the slack,
-    // alpha = 1, the same P as an update after the max).  Boundary tiles,
-    // and whole tiles whose max moved a reference (a row's first tile, a
-    // jump of its max), recompute the scores from LDS and take the masked,
-    // max-first update; no score then stays live beside the P values.
-    // Both branches are uniform over the workgroup or the wave.
-    const bool boundary = has_pad || t * kTileKeys < lo_last || t * kTileKeys + kTileKeys - 1 > p_first;
-    bool moved = true;
-    u32x2 pb[RT][4];
-    if (!boundary) {
-      float m_use[RT], mxl[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        m_use[rt] = m[rt] == -INFINITY ? 0.f : m[rt];
-        mxl[rt] = -INFINITY;
-      }
-      auto p_fast = [&](int sub) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mxl[rt] = fmaxf(mxl[rt], sacc[rt][sub][i]);
-          pb[rt][sub] = p_subtile(rt, sub, m_use[rt]);
-          // Pinned here: otherwise the compiler sinks the exps below the
-          // branch that uses them, past the products they should overlap.
-          asm volatile("" : "+v"(pb[rt][sub].x), "+v"(pb[rt][sub].y));
-        }
-      };
-      qk_subtile(0);
-#pragma unroll
-      for (int sub = 1; sub < 4; ++sub) {
-        qk_subtile(sub);
-        p_fast(sub - 1);
-      }
-      p_fast(3);
-      bool mv = false;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const float mx = max_over_lane_groups(mxl[rt]);
-        mv = mv || next_reference(m[rt], mx * scale) != m[rt];
-      }
-      moved = __ballot(mv) != 0;
-    }
-    if (moved) {
+    // sacc[rt][sub][i] = raw score of key t*64 + sub*16 + 4*grp + i for this
+    // lane's row of row tile rt.  The mask branch is uniform over the
+    // workgroup.
+    if (has_pad || t * kTileKeys < lo_last || t * kTileKeys + kTileKeys - 1 > p_first) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub) sacc[rt][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-      for (int sub = 0; sub < 4; ++sub) qk_subtile(sub);
-      if (boundary) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int j = t * kTileKeys + sub * 16 + 4 * grp + i;
-              const bool vis = j >= lo_row[rt] && j <= hi_row[rt];
-              sacc[rt][sub][i] = vis ? sacc[rt][sub][i] : -INFINITY;
-              if constexpr (COUNT) cnt[rt] += vis ? 1 : 0;
-            }
-      }
-      softmax_tile();
+          for (int i = 0; i < 4; ++i) {
+            const int j = t * kTileKeys + sub * 16 + 4 * grp + i;
+            const bool vis = j >= lo_row[rt] && j <= hi_row[rt];
+            sacc[rt][sub][i] = vis ? sacc[rt][sub][i] : -INFINITY;
+            if constexpr (COUNT) cnt[rt] += vis ? 1 : 0;
+          }
     } else {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        alpha[rt] = 1.f;
-        pt[rt][0] = cat(pb[rt][0], pb[rt][1]);
-        pt[rt][1] = cat(pb[rt][2], pb[rt][3]);
-      }
+      for (int rt = 0; rt < RT; ++rt)
+        if constexpr (COUNT) cnt[rt] += 16;
     }
-    if constexpr (COUNT) {
-      if (!boundary) {
+    u32x4 pt[RT][2];
+    float alpha[RT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) cnt[rt] += 16;
+    for (int rt = 0; rt < RT; ++rt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[rt][sub][i]);
+      mx = max_over_lane_groups(mx);
+      const float m_new = next_reference(m[rt], mx * scale);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      alpha[rt] = fast_exp2(m[rt] - m_use);
+      u32x2 pb[4];
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(__builtin_fmaf(sacc[rt][sub][i], scale, -m_use));
+        pb[sub] = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+      }
+      pt[rt][0] = cat(pb[0], pb[1]);
+      pt[rt][1] = cat(pb[2], pb[3]);
+      m[rt] = m_new;
+      if (__ballot(alpha[rt] != 1.f)) {
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn) o[rt][nn] *= alpha[rt];
       }
     }
 
