@@ -229,7 +229,7 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
   // Split-KV part: decode and verify, and a mixed call's short sequences.
   if (entry != DIFFKV_ENTRY_PREFILL) {
     const diffkv_attn_desc sd = split_part_desc(*d, entry);
-    const SplitPlan plan = plan_split(sd, window, kSplitSlotsPerCu);
+    const SplitPlan plan = plan_split(sd, window, kLaunchSlots);
     if (!plan.direct && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
       return DIFFKV_WORKSPACE_TOO_SMALL;
     SplitArgs sa = a;
@@ -411,7 +411,7 @@ int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry) {
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window) {
   if (validate_desc(desc, entry) != DIFFKV_OK) return 0;
   if (entry == DIFFKV_ENTRY_PREFILL) return 1;
-  return plan_split(split_part_desc(*desc, entry), window, kSplitSlotsPerCu).max_chunks;
+  return plan_split(split_part_desc(*desc, entry), window, kLaunchSlots).max_chunks;
 }
 
 int diffkv_attn_profile_next_call(hipEvent_t start, hipEvent_t stop) {

@@ -70,12 +70,27 @@ inline long long max_keys_bound(const diffkv_attn_desc& d, int window) {
 #ifndef DIFFKV_SPLIT_SLOTS_PER_CU
 #define DIFFKV_SPLIT_SLOTS_PER_CU DIFFKV_SPLIT_WAVES_PER_EU
 #endif
+#ifndef DIFFKV_SPLIT_SLOTS_PER_CU_64
+#define DIFFKV_SPLIT_SLOTS_PER_CU_64 1
+#endif
 #ifndef DIFFKV_MIN_TILES_PER_SPLIT
 #define DIFFKV_MIN_TILES_PER_SPLIT 4
 #endif
 template <bool FP8> constexpr int kSplitStages = FP8 ? DIFFKV_FP8_STAGES : DIFFKV_BF16_STAGES;
 constexpr int kSplitWavesPerEu = DIFFKV_SPLIT_WAVES_PER_EU;
 constexpr int kSplitSlotsPerCu = DIFFKV_SPLIT_SLOTS_PER_CU;
+// Workgroups of 64 query rows (4 row tiles: a verify block at GQA 8 or
+// more) over a bf16 cache plan one chunk per CU instead: each workgroup
+// then has every SIMD to itself for its four times larger products, and the
+// fewer, longer chunks halve the partials the merge reads (verify at
+// 40K-50K tokens: 29.8 vs 30.5 us for the split kernel, 34.7 vs 35.7 us for
+// the call).  FP8 caches keep two: the widening adds VALU work per tile
+// that a second workgroup hides (the split part of a mixed FP8 batch took
+// 148 instead of 121 us with one).
+constexpr int kSplitSlotsPerCu64 = DIFFKV_SPLIT_SLOTS_PER_CU_64;
+// plan_split's wgs_per_cu for a launch: slots chosen from the row tiles and
+// the cache format.
+constexpr int kLaunchSlots = -1;
 
 // Split plan from host bounds.  The kernels cut the keys on the device
 // (balanced chunks of C = max(kMinTilesPerSplit, ceil(T / slots)) tiles, T
@@ -96,6 +111,8 @@ inline SplitPlan plan_split(const diffkv_attn_desc& d, int window,
   const long long rows_pair = (long long)d.max_q_len * G;
   p.row_tiles = split_row_tiles((int)(rows_pair < 64 ? rows_pair : 64));
   p.rows = 16 * p.row_tiles;
+  if (wgs_per_cu == kLaunchSlots)
+    wgs_per_cu = p.row_tiles == 4 && d.kv_dtype == DIFFKV_KV_BF16 ? kSplitSlotsPerCu64 : kSplitSlotsPerCu;
   p.n_qtiles = ceil_div(rows_pair, p.rows);
   const long long pairs = (long long)d.batch * p.n_qtiles;
   const long long max_tiles = ceil_div(max_keys_bound(d, window), kTileKeys) + 1;
