@@ -19,6 +19,10 @@ steps alone (HIP events around the K calls, no per-call instrumentation).
 `roofline` is the main attention kernel alone: a second pass of the same K
 calls has the library's dispatch stamp each main kernel with HIP events
 (diffkv_attn_profile_next_call); their mean is the kernel's duration.
+`roofline.stream_read` (decode and verify) is the achievable-bandwidth
+reference at the kernel's own byte count: a plain streaming read of that many
+bytes in one launch, cold, timed the same way; `kernel_frac_of_stream` is the
+attention kernel's rate as a fraction of it.
 `cpu_baseline` times the FP64 oracle on the host on a bounded sample.
 `extra` carries the other workloads measured the same way (mixed_batch: one
 serving step mixing a prefill chunk, verify blocks and decodes;
@@ -145,7 +149,8 @@ def kernel_source_sha():
     import glob
     from paged_asymmetric_head_amd.build import command
     h = hashlib.sha256()
-    paths = sorted(glob.glob(os.path.join(ROOT, "paged_asymmetric_head_amd", "csrc", "*")))
+    paths = sorted(p for p in glob.glob(os.path.join(ROOT, "paged_asymmetric_head_amd", "csrc", "*"))
+                   if os.path.basename(p) != "stream_read.hip")
     paths.append(os.path.join(ROOT, "include", "diffkv_attn.h"))
     for path in paths:
         with open(path, encoding="utf-8") as f:
@@ -332,6 +337,67 @@ def measure_context_split(steps, warmup, events, parts=2, target_bytes=1 << 30):
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                          "kernel": "split_attn_kernel (context partial)", "kernel_ms": round(ms, 5),
                          "work_per_launch": kv_bytes}}
+
+
+# Launch shapes tried for the streaming-read reference: (workgroups, loads
+# in flight per thread).
+STREAM_SHAPES = [(b, u) for b in (512, 1024, 2048, 4096, 8192) for u in (4, 8)]
+
+
+def stream_read_reference(nbytes, steps, events, target_bytes=1 << 30):
+    """Achievable read bandwidth at one size: a plain grid-stride 16-byte read
+    of `nbytes` (libdiffkv_stream.so), timed like the attention kernels (HIP
+    events around each launch), cold in L2 and the Infinity Cache (copies
+    walked in turn, more than 1 GiB in all); the fastest of a few launch
+    shapes.  Context for the HBM fraction: what one launch of plain reads of
+    that many bytes reaches on this GPU."""
+    import torch
+    path = os.path.join(ROOT, "paged_asymmetric_head_amd", "libdiffkv_stream.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    lib.diffkv_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p]
+    lib.diffkv_stream_read.restype = ctypes.c_int
+    nbytes = nbytes // 16 * 16
+    copies = max(2, math.ceil(target_bytes / nbytes) + 1)
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i % 251) for i in range(copies)]
+    sink = torch.empty(max(b for b, _ in STREAM_SHAPES) * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    best = None
+    for blocks, unroll in STREAM_SHAPES:
+        def launch(k):
+            st = lib.diffkv_stream_read(bufs[k % copies].data_ptr(), nbytes, sink.data_ptr(), blocks, unroll,
+                                        stream)
+            if st != 0:
+                raise RuntimeError(f"diffkv_stream_read: status {st}")
+        for k in range(5):
+            launch(k)
+        torch.cuda.synchronize()
+        pairs = [(events.create(), events.create()) for _ in range(steps)]
+        for k in range(steps):
+            events.record(pairs[k][0], stream)
+            launch(k)
+            events.record(pairs[k][1], stream)
+        torch.cuda.synchronize()
+        ms = sum(events.elapsed_ms(a, b) for a, b in pairs) / steps
+        if best is None or ms < best[2]:
+            best = (blocks, unroll, ms)
+    del bufs, sink
+    torch.cuda.empty_cache()
+    blocks, unroll, ms = best
+    return {"bytes": nbytes, "kernel_ms": round(ms, 5), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "blocks": blocks, "loads_per_thread": unroll,
+            "kernel": "stream_read_kernel (libdiffkv_stream.so)"}
+
+
+def with_stream_reference(roof, steps, events):
+    """Adds the streaming-read reference at the kernel's own byte count to an
+    HBM-bound roofline record, and the kernel's fraction of it."""
+    ref = stream_read_reference(roof["work_per_launch"], steps, events)
+    ref["kernel_frac_of_stream"] = round(roof["achieved"] / ref["gbs"], 4)
+    roof["stream_read"] = ref
+    return roof
 
 
 COPY_BYTES = 256 << 20
@@ -537,6 +603,9 @@ def main():
         "kernel_source_sha": sha,
     }
     del m
+    if head["roofline"]["bound"] == "hbm":
+        print(f"[bench] {name}: streaming-read reference", file=sys.stderr, flush=True)
+        with_stream_reference(result["roofline"], args.steps, events)
     if not args.no_extra:
         extra = {}
         for other in ("verify_long", "swa_sinks_fp8_p1", "swa_sinks_fp8_p128", "chunked_prefill",
@@ -546,6 +615,8 @@ def main():
             print(f"[bench] {other}: generating and measuring", file=sys.stderr, flush=True)
             mo = measure(other, args.extra_steps, 5, events)
             extra[other] = summary(mo, sha, other)
+            if other == "verify_long":
+                with_stream_reference(extra[other]["roofline"], args.extra_steps, events)
             del mo
             torch.cuda.empty_cache()
         for other in KV_WRITE_OF:

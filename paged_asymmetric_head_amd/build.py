@@ -1,4 +1,6 @@
-"""Builds libdiffkv_attn.so in-tree with hipcc for gfx950.
+"""Builds libdiffkv_attn.so (the attention library) and libdiffkv_stream.so
+(the streaming-read reference the benchmark quotes beside HBM peak) in-tree
+with hipcc for gfx950.
 
     python -m paged_asymmetric_head_amd.build
 
@@ -16,6 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUTPUT = os.path.join(HERE, "libdiffkv_attn.so")
 SOURCES = [os.path.join(CSRC, "diffkv_attn.hip")]
+STREAM_OUTPUT = os.path.join(HERE, "libdiffkv_stream.so")
+STREAM_SOURCES = [os.path.join(CSRC, "stream_read.hip")]
 ARCH = "gfx950"
 
 
@@ -26,23 +30,29 @@ def hipcc():
     return "hipcc"
 
 
-def command(output=OUTPUT, extra=()):
+def command(output=OUTPUT, extra=(), sources=SOURCES):
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}",
-            *extra, "-o", output, *SOURCES]
+            *extra, "-o", output, *sources]
 
 
-def build(verbose=False):
-    tmp = OUTPUT + ".tmp"
-    cmd = command(tmp)
+def _compile(output, sources, verbose):
+    tmp = output + ".tmp"
+    cmd = command(tmp, sources=sources)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with status {res.returncode}")
-    os.replace(tmp, OUTPUT)
+    os.replace(tmp, output)
+
+
+def build(verbose=False):
+    """Compile both libraries; returns the attention library's path."""
+    _compile(OUTPUT, SOURCES, verbose)
+    _compile(STREAM_OUTPUT, STREAM_SOURCES, verbose)
     return OUTPUT
 
 

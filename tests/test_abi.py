@@ -178,3 +178,22 @@ def test_partial_and_combine_reject_before_touching_the_gpu(lib):
     assert c(2, 10, 4, fake, fake, None, fake, None, None) == B.INVALID_ARGUMENT   # rows % Hq
     assert c(65, 8, 4, fake, fake, None, fake, None, None) == B.UNSUPPORTED
     assert c(2, 8, 4, None, fake, None, fake, None, None) == B.INVALID_ARGUMENT
+
+
+def test_stream_reference_library_loads_and_rejects_bad_arguments():
+    """The streaming-read reference the benchmark quotes (its own library,
+    outside the attention ABI) loads, exports its one call, and rejects bad
+    arguments on the host without launching anything."""
+    import ctypes
+    path = os.path.join(ROOT, "paged_asymmetric_head_amd", "libdiffkv_stream.so")
+    lib = ctypes.CDLL(path)
+    fn = lib.diffkv_stream_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    assert fn(None, 16, 16, 1, 4, None) == 1            # null source
+    assert fn(16, 16, None, 1, 4, None) == 1            # null sink
+    assert fn(16, 16, 16, 0, 4, None) == 1              # no workgroups
+    assert fn(16, 17, 16, 1, 4, None) == 1              # not a multiple of 16 bytes
+    assert fn(8, 16, 16, 1, 4, None) == 1               # misaligned source
+    assert fn(16, 16, 16, 1, 5, None) == 1              # unsupported loads per thread
