@@ -29,7 +29,9 @@ serving step mixing a prefill chunk, verify blocks and decodes;
 batched_decode_sym: the decode batch with symmetric 128/128 heads), the paged KV
 write (diffkv_kv_write) on the decode and prefill token counts, and one GPU's
 share of a two-way context split of the decode workload (diffkv_attn_partial
-over half of every sequence's keys, and the diffkv_attn_combine merge).
+over half of every sequence's keys, and the diffkv_attn_combine merge), and a
+sweep of the decode shape over context lengths (2K-64K tokens per sequence)
+with the fit kernel time = a + bytes / B.
 """
 
 import argparse
@@ -63,7 +65,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batched_decode",
-                    choices=sorted(ENTRY_OF) + sorted(KV_WRITE_OF) + ["context_split_decode"],
+                    choices=sorted(ENTRY_OF) + sorted(KV_WRITE_OF) + ["context_split_decode", "decode_sweep"],
                     help="attention workload for the headline line; a KV-write or context-split "
                          "name prints that measurement's own line instead")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
@@ -343,6 +345,78 @@ def measure_context_split(steps, warmup, events, parts=2, target_bytes=1 << 30):
 # in flight per thread).
 STREAM_SHAPES = [(b, u) for b in (512, 1024, 2048, 4096, 8192) for u in (4, 8)]
 
+# Decode context sweep: the batched-decode shape (32 sequences, Hq 8 / Hkv 1,
+# QK 192 / V 128, page 128, bf16) at these lower bounds of the context range
+# [L, 9L/8], to fit time = a + bytes / B over context length.
+SWEEP_CONTEXTS = (2048, 8192, 16384, 32768, 65536)
+
+
+def measure_decode_sweep(steps, warmup, events, contexts=SWEEP_CONTEXTS, target_bytes=1 << 30,
+                         shuffle=True):
+    """The decode kernel over context lengths, for timing only: K/V are random
+    bf16 values drawn on the device (no parity check here; the seeded
+    workloads are checked by the tests), pages in a random permutation, the
+    same launch path and cold-cache rotation as the other workloads.  Returns
+    per-context kernel times and the least-squares fit of kernel time =
+    a + bytes / B."""
+    import numpy as np
+    import torch
+    from paged_asymmetric_head_amd import binding as B
+    batch, hq, hkv, dqk, dv, P = 32, 8, 1, 192, 128, 128
+    rng = np.random.default_rng(11)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for L0 in contexts:
+        lens = rng.integers(L0, L0 + L0 // 8 + 1, size=batch).astype(np.int32)
+        pages = (lens + P - 1) // P
+        num_pages = int(pages.sum())
+        stride = int(-(-int(lens.max()) // P))
+        perm = (rng.permutation(num_pages) if shuffle else np.arange(num_pages)).astype(np.int32)
+        bt = np.full((batch, stride), -1, dtype=np.int32)
+        off = 0
+        for b in range(batch):
+            bt[b, :pages[b]] = perm[off:off + pages[b]]
+            off += int(pages[b])
+        pool = num_pages * P * hkv * (dqk + dv) * 2
+        layers = max(1, min(16, math.ceil(target_bytes / pool)))
+        caches = [(torch.randn((num_pages, P, hkv, dqk), generator=gen, device="cuda").to(torch.bfloat16),
+                   torch.randn((num_pages, P, hkv, dv), generator=gen, device="cuda").to(torch.bfloat16))
+                  for _ in range(layers)]
+        q = torch.randn((batch, hq, dqk), generator=gen, device="cuda").to(torch.bfloat16)
+        bt_d = torch.from_numpy(bt).cuda()
+        lens_d = torch.from_numpy(lens).cuda()
+        qlens_d = torch.ones(batch, dtype=torch.int32, device="cuda")
+        out = torch.empty((batch, hq, dv), dtype=torch.bfloat16, device="cuda")
+        d = B.AttnDesc(batch=batch, num_q_heads=hq, num_kv_heads=hkv, head_dim_qk=dqk, head_dim_v=dv,
+                       page_size=P, num_pages=num_pages, block_table_stride=stride,
+                       max_seq_len=int(lens.max()), max_q_len=1, total_q=batch, kv_dtype=B.KV_BF16,
+                       force_num_splits=0)
+        nbytes = B.diffkv_attn_workspace_bytes(d, B.ENTRIES["decode"])
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        calls = [B.prepared_call("diffkv_attn_decode", d, q, k, v, bt_d, lens_d, qlens_d, 0, None, 1.0, 1.0,
+                                 1.0 / math.sqrt(dqk), out, None, None, ws, nbytes, stream)
+                 for k, v in caches]
+        total_ms, _, kern = time_calls(calls, steps, warmup, events, stream)
+        if not bool(torch.isfinite(out.float()).all()):
+            raise RuntimeError(f"decode sweep at {L0}: non-finite output")
+        kv_bytes = int(lens.astype(np.int64).sum()) * hkv * (dqk + dv) * 2
+        ms = sum(kern) / len(kern)
+        rows.append({"context_lo": int(L0), "kv_bytes": kv_bytes, "kernel_ms": round(ms, 5),
+                     "step_ms": round(total_ms / steps, 5),
+                     "kernel_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+                     "frac": round(kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "layers": layers})
+        del caches, calls, ws, out
+        torch.cuda.empty_cache()
+    x = np.array([r["kv_bytes"] for r in rows], dtype=np.float64)
+    y = np.array([r["kernel_ms"] * 1e-3 for r in rows], dtype=np.float64)
+    slope, icept = np.polyfit(x, y, 1)
+    return {"shape": "batch 32, Hq 8 / Hkv 1, QK 192 / V 128, page 128, bf16, contexts uniform in [L, 9L/8]",
+            "data": "random bf16 K/V drawn on the device (timing only)", "points": rows,
+            "fit_kernel_ms": {"a_us": round(icept * 1e6, 2), "B_gbs": round(1.0 / slope / 1e9, 1)}}
+
+
 
 def stream_read_reference(nbytes, steps, events, target_bytes=1 << 30):
     """Achievable read bandwidth at one size: a plain grid-stride 16-byte read
@@ -575,6 +649,7 @@ def main():
     if name not in ENTRY_OF:
         print(f"[bench] {name}: generating and measuring", file=sys.stderr, flush=True)
         res = (measure_kv_write(name, args.steps, args.warmup, events) if name in KV_WRITE_OF
+               else measure_decode_sweep(args.steps, args.warmup, events) if name == "decode_sweep"
                else measure_context_split(args.steps, args.warmup, events))
         print(json.dumps({"workload": name, "steps": args.steps, "warmup": args.warmup,
                           "kernel_source_sha": sha, **res}), flush=True)
@@ -625,6 +700,9 @@ def main():
             torch.cuda.empty_cache()
         print("[bench] context_split_decode: generating and measuring", file=sys.stderr, flush=True)
         extra["context_split_decode"] = measure_context_split(args.extra_steps, 5, events)
+        torch.cuda.empty_cache()
+        print("[bench] decode_sweep: generating and measuring", file=sys.stderr, flush=True)
+        extra["decode_sweep"] = measure_decode_sweep(args.extra_steps, 5, events)
         torch.cuda.empty_cache()
         result["extra"] = extra
     if args.copy_calibration:

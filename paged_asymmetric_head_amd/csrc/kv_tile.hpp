@@ -28,13 +28,17 @@ constexpr int kVLdsElems = kTileKeys * kVLdsStride;
 // source of every load whose key lies outside the range a tile may read.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[16];
 
-template <bool FP8, bool UPAGE, int DQK, int NT = 256>
+// NT threads move TK keys of each 64-key tile: all of it (TK = 64), or, for
+// a loader private to one wave (NT = 64), the slice of TK keys starting at
+// key_off that only this wave reads, so no barrier orders it against the
+// other waves.
+template <bool FP8, bool UPAGE, int DQK, int NT = 256, int TK = kTileKeys>
 struct KvTile {
   static constexpr int ESZ = FP8 ? 1 : 2;
   static constexpr int K_UPR = DQK * ESZ / 16;          // 16-byte units per K row
   static constexpr int V_UPR = kHeadDimV * ESZ / 16;
-  static constexpr int K_UNITS = kTileKeys * K_UPR;     // units per tile
-  static constexpr int V_UNITS = kTileKeys * V_UPR;
+  static constexpr int K_UNITS = TK * K_UPR;            // units per tile (slice)
+  static constexpr int V_UNITS = TK * V_UPR;
   static constexpr int KU = (K_UNITS + NT - 1) / NT;    // units per thread per tile
   static constexpr int VU = (V_UNITS + NT - 1) / NT;
   static constexpr int NPK = UPAGE ? 1 : KU;            // page ids held per thread per tile
@@ -53,20 +57,21 @@ struct KvTile {
   const int32_t* bt;         // this sequence's block-table row
   size_t k_slot_bytes, v_slot_bytes;   // Hkv rows per slot
   int lp, pmask, kv_lo, kv_hi, t_last, tid;
+  int koff;                  // first key of this loader's slice in each tile
   // Large pages: byte offset of each of this thread's units from the tile's
   // first slot (the tile lies inside one page, so rows are slot-contiguous).
   uint32_t k_off[UPAGE ? KU : 1], v_off[UPAGE ? VU : 1];
 
   __device__ __forceinline__ KvTile(const uint8_t* k_cache, const uint8_t* v_cache,
                                     const int32_t* bt_row, int hkv, int g, int log2_page,
-                                    int lo, int hi, int t_end, int thread)
+                                    int lo, int hi, int t_end, int thread, int key_off = 0)
       : k_head(k_cache + (size_t)g * DQK * ESZ),
         v_head(v_cache + (size_t)g * kHeadDimV * ESZ),
         bt(bt_row),
         k_slot_bytes((size_t)hkv * DQK * ESZ),
         v_slot_bytes((size_t)hkv * kHeadDimV * ESZ),
         lp(log2_page), pmask((1 << log2_page) - 1), kv_lo(lo), kv_hi(hi), t_last(t_end - 1),
-        tid(thread) {
+        tid(thread), koff(key_off) {
     if constexpr (UPAGE) {
 #pragma unroll
       for (int k = 0; k < KU; ++k) k_off[k] = (uint32_t)(k_row(k) * k_slot_bytes + k_piece(k) * 16);
@@ -75,10 +80,12 @@ struct KvTile {
     }
   }
 
-  // Units past the tile (k_has false) map to row 0 and read the zero row.
-  __device__ __forceinline__ int k_row(int k) const { return k_has(k) ? (tid + NT * k) / K_UPR : 0; }
+  // Key of unit k within the 64-key tile (this loader's slice starts at
+  // koff); units past the slice (k_has false) map to its first key and read
+  // the zero row.
+  __device__ __forceinline__ int k_row(int k) const { return koff + (k_has(k) ? (tid + NT * k) / K_UPR : 0); }
   __device__ __forceinline__ int k_piece(int k) const { return (tid + NT * k) % K_UPR; }
-  __device__ __forceinline__ int v_key(int k) const { return v_has(k) ? (tid + NT * k) / V_UPR : 0; }
+  __device__ __forceinline__ int v_key(int k) const { return koff + (v_has(k) ? (tid + NT * k) / V_UPR : 0); }
   __device__ __forceinline__ int v_piece(int k) const { return (tid + NT * k) % V_UPR; }
   __device__ __forceinline__ bool readable(int j) const { return j >= kv_lo && j < kv_hi; }
 

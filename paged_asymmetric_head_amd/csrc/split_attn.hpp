@@ -28,6 +28,8 @@
 // tile is converted into LDS and multiplied.
 #pragma once
 
+#include <type_traits>
+
 #include "kv_tile.hpp"
 
 namespace diffkv {
@@ -204,7 +206,13 @@ void split_attn_kernel(const SplitArgs a) {
   constexpr int KW = 4 / RT;                 // waves splitting the keys of one row tile
   constexpr int SUBS = kTileKeys / 16 / KW;  // 16-key subtiles per wave per tile
   constexpr int QC = DQK / 32;               // 32-dim contraction steps of QK^T
-  using IO = KvTile<FP8, UPAGE, DQK>;
+  // 16-row tiles: each wave reads only its own 16 keys of a tile, so it
+  // gathers them itself into its own LDS rows and streams without waiting
+  // for the other waves (no barrier per tile; a wave's LDS reads and writes
+  // stay in program order).  Larger row tiles share every key between waves
+  // and gather the tile together, with barriers.
+  constexpr bool WAVE_LOCAL = RT == 1;
+  using IO = std::conditional_t<WAVE_LOCAL, KvTile<FP8, UPAGE, DQK, 64, 16>, KvTile<FP8, UPAGE, DQK>>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kKLdsElems<DQK> + kVLdsElems];
   uint16_t* k_lds = lds;
   uint16_t* v_lds = lds + kKLdsElems<DQK>;
@@ -264,7 +272,7 @@ void split_attn_kernel(const SplitArgs a) {
   }
 
   const IO io(a.k_cache, a.v_cache, a.block_table + (size_t)b * a.bt_stride, a.hkv, g,
-              a.log2_page, kv_lo, kv_hi, t_end, tid);
+              a.log2_page, kv_lo, kv_hi, t_end, WAVE_LOCAL ? lane : tid, WAVE_LOCAL ? 16 * wave : 0);
 
   // NS tiles of K/V in flight in registers; page ids NS tiles ahead of the
   // data they address.
@@ -408,9 +416,9 @@ void split_attn_kernel(const SplitArgs a) {
   for (int t = t_begin; t < t_end; t += NS) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      __syncthreads();
+      if constexpr (!WAVE_LOCAL) __syncthreads();
       io.store(st[i], k_lds, v_lds);
-      __syncthreads();
+      if constexpr (!WAVE_LOCAL) __syncthreads();
       io.fetch_data(t + i + NS, pg[i], st[i]);
       io.fetch_pages(t + i + 2 * NS, pg[i]);
       if (t + i < t_end) compute_tile(t + i);
