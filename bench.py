@@ -412,9 +412,13 @@ def measure_decode_sweep(steps, warmup, events, contexts=SWEEP_CONTEXTS, target_
     x = np.array([r["kv_bytes"] for r in rows], dtype=np.float64)
     y = np.array([r["kernel_ms"] * 1e-3 for r in rows], dtype=np.float64)
     slope, icept = np.polyfit(x, y, 1)
+    # The streaming-read reference at the longest context's byte count.
+    ref = stream_read_reference(rows[-1]["kv_bytes"], steps, events)
+    ref["kernel_frac_of_stream"] = round(rows[-1]["kernel_gbs"] / ref["gbs"], 4)
     return {"shape": "batch 32, Hq 8 / Hkv 1, QK 192 / V 128, page 128, bf16, contexts uniform in [L, 9L/8]",
             "data": "random bf16 K/V drawn on the device (timing only)", "points": rows,
-            "fit_kernel_ms": {"a_us": round(icept * 1e6, 2), "B_gbs": round(1.0 / slope / 1e9, 1)}}
+            "fit_kernel_ms": {"a_us": round(icept * 1e6, 2), "B_gbs": round(1.0 / slope / 1e9, 1)},
+            "stream_read_longest": ref}
 
 
 
