@@ -78,7 +78,8 @@ __device__ __forceinline__ void split_tiles(int kv_lo, int kv_hi, int S, int s, 
 // Balanced split plan.  The keys a (sequence, query tile) pair sees span
 // nt 64-key tiles; over the pairs of the launch (sequences with q_lo <=
 // q_len <= q_hi) they total T.  With C = max(kMinTilesPerSplit, ceil(T /
-// slots)) a pair is cut into k = ceil(nt / C) chunks of equal tile counts
+// slots)), lengthened while the chunks would not fit one resident round of
+// slots, a pair is cut into k = ceil(nt / C) chunks of equal tile counts
 // (force_splits fixes k instead), and chunk ids number the chunks pair by
 // pair in (sequence, query tile) order.  Every split workgroup derives the
 // same plan from seq_lens and q_lens (the first chunk of each pair records
@@ -144,33 +145,62 @@ struct SplitPlanner {
     }
     T = wave_sum_int(T);
     C = max(kMinTilesPerSplit, (T + a.slots - 1) / a.slots);
+    // Rounding every pair up to whole chunks can give more chunks than the
+    // slots of one resident round (up to slots + pairs, which the grid
+    // covers); the chunks past the round would start only when others end
+    // and run as a tail after them (decode at 64K tokens per sequence: 524
+    // chunks for 512 slots).  Lengthen the chunks by about 3% a step until
+    // they fit; a few steps at most, none for the usual near-uniform batch.
+    // Up to 64 sequences the check rides on find()'s own prefix sum, which
+    // already counts every chunk; larger batches count here.
+    if (a.batch > 64)
+      for (int it = 0; it < kFitSteps && total_chunks() > a.slots; ++it) C += max(1, C >> 5);
+  }
+  static constexpr int kFitSteps = 8;
+
+  // Chunks of the whole launch at the current chunk length C.
+  __device__ __forceinline__ int total_chunks() const {
+    int S = 0;
+    for (int b0 = 0; b0 < a.batch; b0 += 64) {
+      int L = L0, n = n0, klo = lo0, khi = hi0;
+      if (b0 > 0) load(b0, L, n, klo, khi);
+      S += seq_chunks(L, n, klo, khi);
+    }
+    return wave_sum_int(S);
   }
 
   // The pair and chunk of chunk id w, with the sequence's lengths, key
   // bounds and first packed query row; false when w is past the last chunk.
   __device__ __forceinline__ bool find(int w, int& b, int& qt, int& c, int& base, int& k, int& L_b,
-                                       int& n_b, int& klo_b, int& khi_b, int& r0) const {
+                                       int& n_b, int& klo_b, int& khi_b, int& r0) {
     int before = 0;                           // chunks of the earlier passes
     int rows_before = 0;                      // new tokens of the earlier passes
     for (int b0 = 0; b0 < a.batch; b0 += 64) {
       int L = L0, n = n0, klo = lo0, khi = hi0;
       if (b0 > 0) load(b0, L, n, klo, khi);
-      const int kb = seq_chunks(L, n, klo, khi);
       // Inclusive prefix sums over the lanes (chunks, and new tokens for the
       // packed row start).
-      int incl = kb, nincl = n;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        incl += lane_id() >= o ? y : 0;
-      }
-      if (a.q_lens) {
+      auto prefix = [&](int v) {
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(nincl, o, 64);
-          nincl += lane_id() >= o ? y : 0;
+          const int y = __shfl_up(v, o, 64);
+          v += lane_id() >= o ? y : 0;
+        }
+        return v;
+      };
+      int kb = seq_chunks(L, n, klo, khi);
+      int incl = prefix(kb);
+      // One pass holds the whole batch: its count decides whether the
+      // chunks fit one resident round (see init).
+      if (a.batch <= 64 && a.force_splits <= 0) {
+        for (int it = 0; it < kFitSteps && read_lane(incl, 63) > a.slots; ++it) {
+          C += max(1, C >> 5);
+          kb = seq_chunks(L, n, klo, khi);
+          incl = prefix(kb);
         }
       }
+      int nincl = n;
+      if (a.q_lens) nincl = prefix(n);
       const int total = read_lane(incl, 63);
       if (w < before + total) {
         const int owner = __builtin_ctzll(__ballot(before + incl > w));
