@@ -1,8 +1,9 @@
 """GPU parity of the balanced split plan: batches whose sequences differ
 widely in length, so some (sequence, query tile) pairs get one chunk (written
 directly, skipped by the merge) and others many, and batches of more than 64
-sequences (the plan walks the batch 64 sequences per pass).  count_out checks
-that every visible key is combined exactly once.
+sequences (the plan walks the batch 64 sequences per pass), and batches whose
+chunks are lengthened to fit one resident round.  count_out checks that every
+visible key is combined exactly once.
 """
 
 import numpy as np
@@ -41,3 +42,18 @@ def test_mixed_with_long_sequences_between_short_ones():
                             page_size=128, kv_dtype="bf16", window=512, sinks=True,
                             write_align=128)
     check_call(DeviceInputs(inp), "mixed", "mixed heterogeneous")
+
+
+@pytest.mark.parametrize("batch,seed,lo,hi,hq,hkv,page", [(48, 39, 2000, 6000, 8, 1, 128),
+                                                         (100, 1, 500, 3000, 4, 2, 16)],
+                         ids=["one_pass", "two_passes"])
+def test_chunks_lengthened_to_fit_one_round(batch, seed, lo, hi, hq, hkv, page):
+    """Lengths whose per-pair rounding gives more chunks than the slots of one
+    resident round (534 for 512 with 48 sequences; 300 for 256 per KV head
+    with 100 sequences, whose check runs in the plan's multi-pass count): the
+    plan lengthens the chunks until they fit, and every workgroup and the
+    merge must agree on the lengthened plan."""
+    lens = [int(x) for x in np.random.default_rng(seed).integers(lo, hi, size=batch)]
+    inp = make_paged_inputs(405 + batch, seq_lens=lens, q_lens=1, num_q_heads=hq, num_kv_heads=hkv,
+                            page_size=page, kv_dtype="bf16", sinks=True)
+    check_call(DeviceInputs(inp), "decode", f"{batch} sequences, chunks fitted to one round")
