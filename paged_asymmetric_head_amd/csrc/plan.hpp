@@ -55,9 +55,9 @@ inline long long max_keys_bound(const diffkv_attn_desc& d, int window) {
 // for, which is also the number of its 256-thread workgroups resident per
 // CU.  Both K/V formats keep a single register stage: with a resident round
 // of workgroups that is enough loads in flight for HBM, and deeper stages
-// measured slower (the opening burst of loads delays every workgroup's
-// first tile).  Two workgroups per CU for every page size (three measured no
-// better).
+// measured slower at the common sizes (the opening burst of loads delays
+// every workgroup's first tile; two bf16 stages cost 2% on decode at 8K
+// tokens per sequence for 2% at 64K).  Two workgroups per CU (three spill).
 #ifndef DIFFKV_BF16_STAGES
 #define DIFFKV_BF16_STAGES 1
 #endif
