@@ -18,7 +18,8 @@ One JSON line is printed.  `value` and `ms_per_step` come from the timed
 steps alone (HIP events around the K calls, no per-call instrumentation).
 `roofline` is the main attention kernel alone: a second pass of the same K
 calls has the library's dispatch stamp each main kernel with HIP events
-(diffkv_attn_profile_next_call); their mean is the kernel's duration.
+(diffkv_attn_profile_next_call); their mean is the kernel's duration (the
+median is reported beside it).
 `roofline.stream_read` (decode and verify) is the achievable-bandwidth
 reference at the kernel's own byte count: a plain streaming read of that many
 bytes in one launch, cold, timed the same way; `kernel_frac_of_stream` is the
@@ -561,11 +562,13 @@ def roofline(m, sha, name):
         return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic, "kernel": KERNEL_OF_ENTRY[m["entry"]],
-                "kernel_ms": round(ms, 5), "work_per_launch": w["flops"]}
+                "kernel_ms": round(ms, 5), "kernel_ms_median": round(m["kernel_ms_median"], 5),
+                "work_per_launch": w["flops"]}
     achieved = w["kv_bytes"] / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": KERNEL_OF_ENTRY[m["entry"]], "kernel_ms": round(ms, 5),
+            "kernel_ms_median": round(m["kernel_ms_median"], 5),
             "work_per_launch": w["kv_bytes"]}
 
 
