@@ -32,7 +32,8 @@ write (diffkv_kv_write) on the decode and prefill token counts, and one GPU's
 share of a two-way context split of the decode workload (diffkv_attn_partial
 over half of every sequence's keys, and the diffkv_attn_combine merge), and a
 sweep of the decode shape over context lengths (2K-64K tokens per sequence)
-with the fit kernel time = a + bytes / B.
+with the fit kernel time = a + bytes / B, and a sweep of the long-verify shape
+over batch sizes (4-32 sequences at 40K-50K tokens).
 """
 
 import argparse
@@ -66,7 +67,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batched_decode",
-                    choices=sorted(ENTRY_OF) + sorted(KV_WRITE_OF) + ["context_split_decode", "decode_sweep"],
+                    choices=sorted(ENTRY_OF) + sorted(KV_WRITE_OF) + ["context_split_decode", "decode_sweep",
+                                                                       "verify_sweep"],
                     help="attention workload for the headline line; a KV-write or context-split "
                          "name prints that measurement's own line instead")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
@@ -352,6 +354,89 @@ STREAM_SHAPES = [(b, u) for b in (512, 1024, 2048, 4096, 8192) for u in (4, 8)]
 SWEEP_CONTEXTS = (2048, 8192, 16384, 32768, 65536)
 
 
+def _random_paged_call(lens, q_len, rng, gen, stream, target_bytes, shuffle=True):
+    """Prepared C-ABI calls (decode for q_len 1, verify otherwise) over random
+    bf16 K/V drawn on the device, Hq 8 / Hkv 1, QK 192 / V 128, page 128, the
+    pages in a random permutation, replicated into enough copies to pass
+    target_bytes; returns (calls, output tensor, KV bytes of the visible keys)."""
+    import numpy as np
+    import torch
+    from paged_asymmetric_head_amd import binding as B
+    hq, hkv, dqk, dv, P = 8, 1, 192, 128, 128
+    batch = len(lens)
+    pages = (lens + P - 1) // P
+    num_pages = int(pages.sum())
+    stride = int(-(-int(lens.max()) // P))
+    perm = (rng.permutation(num_pages) if shuffle else np.arange(num_pages)).astype(np.int32)
+    bt = np.full((batch, stride), -1, dtype=np.int32)
+    off = 0
+    for b in range(batch):
+        bt[b, :pages[b]] = perm[off:off + pages[b]]
+        off += int(pages[b])
+    pool = num_pages * P * hkv * (dqk + dv) * 2
+    layers = max(1, min(16, math.ceil(target_bytes / pool)))
+    caches = [(torch.randn((num_pages, P, hkv, dqk), generator=gen, device="cuda").to(torch.bfloat16),
+               torch.randn((num_pages, P, hkv, dv), generator=gen, device="cuda").to(torch.bfloat16))
+              for _ in range(layers)]
+    total_q = batch * q_len
+    q = torch.randn((total_q, hq, dqk), generator=gen, device="cuda").to(torch.bfloat16)
+    bt_d = torch.from_numpy(bt).cuda()
+    lens_d = torch.from_numpy(lens).cuda()
+    qlens_d = torch.full((batch,), q_len, dtype=torch.int32, device="cuda")
+    out = torch.empty((total_q, hq, dv), dtype=torch.bfloat16, device="cuda")
+    entry = "decode" if q_len == 1 else "verify"
+    d = B.AttnDesc(batch=batch, num_q_heads=hq, num_kv_heads=hkv, head_dim_qk=dqk, head_dim_v=dv,
+                   page_size=P, num_pages=num_pages, block_table_stride=stride,
+                   max_seq_len=int(lens.max()), max_q_len=q_len, total_q=total_q, kv_dtype=B.KV_BF16,
+                   force_num_splits=0)
+    nbytes = B.diffkv_attn_workspace_bytes(d, B.ENTRIES[entry])
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    calls = [B.prepared_call(f"diffkv_attn_{entry}", d, q, k, v, bt_d, lens_d, qlens_d, 0, None, 1.0, 1.0,
+                             1.0 / math.sqrt(dqk), out, None, None, ws, nbytes, stream)
+             for k, v in caches]
+    kv_bytes = int(lens.astype(np.int64).sum()) * hkv * (dqk + dv) * 2
+    return calls, out, kv_bytes, layers
+
+
+def _sweep_point(calls, out, kv_bytes, layers, steps, warmup, events, stream, label):
+    import torch
+    total_ms, _, kern = time_calls(calls, steps, warmup, events, stream)
+    if not bool(torch.isfinite(out.float()).all()):
+        raise RuntimeError(f"{label}: non-finite output")
+    ms = sum(kern) / len(kern)
+    return {"kv_bytes": kv_bytes, "kernel_ms": round(ms, 5), "step_ms": round(total_ms / steps, 5),
+            "kernel_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac": round(kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "layers": layers}
+
+
+# Verify batch sweep: the long-verify shape (8-token blocks, contexts uniform
+# in [40000, 50000], Hq 8 / Hkv 1, page 128, bf16) at these batch sizes.
+VERIFY_SWEEP_BATCHES = (4, 8, 16, 32)
+
+
+def measure_verify_sweep(steps, warmup, events, batches=VERIFY_SWEEP_BATCHES, target_bytes=1 << 30):
+    """The verify kernel over batch sizes at 40K-50K tokens, for timing only
+    (random bf16 K/V drawn on the device): where the start cost of one launch
+    is spread over more bytes."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(12)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12)
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for batch in batches:
+        lens = rng.integers(40000, 50001, size=batch).astype(np.int32)
+        calls, out, kv_bytes, layers = _random_paged_call(lens, 8, rng, gen, stream, target_bytes)
+        row = _sweep_point(calls, out, kv_bytes, layers, steps, warmup, events, stream, f"verify batch {batch}")
+        rows.append({"batch": batch, **row})
+        del calls, out
+        torch.cuda.empty_cache()
+    return {"shape": "q_len 8 (causal in the block), contexts uniform in [40000, 50000], Hq 8 / Hkv 1, "
+                     "QK 192 / V 128, page 128, bf16",
+            "data": "random bf16 K/V drawn on the device (timing only)", "points": rows}
+
+
 def measure_decode_sweep(steps, warmup, events, contexts=SWEEP_CONTEXTS, target_bytes=1 << 30,
                          shuffle=True):
     """The decode kernel over context lengths, for timing only: K/V are random
@@ -362,53 +447,17 @@ def measure_decode_sweep(steps, warmup, events, contexts=SWEEP_CONTEXTS, target_
     a + bytes / B."""
     import numpy as np
     import torch
-    from paged_asymmetric_head_amd import binding as B
-    batch, hq, hkv, dqk, dv, P = 32, 8, 1, 192, 128, 128
     rng = np.random.default_rng(11)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(11)
     stream = torch.cuda.current_stream().cuda_stream
     rows = []
     for L0 in contexts:
-        lens = rng.integers(L0, L0 + L0 // 8 + 1, size=batch).astype(np.int32)
-        pages = (lens + P - 1) // P
-        num_pages = int(pages.sum())
-        stride = int(-(-int(lens.max()) // P))
-        perm = (rng.permutation(num_pages) if shuffle else np.arange(num_pages)).astype(np.int32)
-        bt = np.full((batch, stride), -1, dtype=np.int32)
-        off = 0
-        for b in range(batch):
-            bt[b, :pages[b]] = perm[off:off + pages[b]]
-            off += int(pages[b])
-        pool = num_pages * P * hkv * (dqk + dv) * 2
-        layers = max(1, min(16, math.ceil(target_bytes / pool)))
-        caches = [(torch.randn((num_pages, P, hkv, dqk), generator=gen, device="cuda").to(torch.bfloat16),
-                   torch.randn((num_pages, P, hkv, dv), generator=gen, device="cuda").to(torch.bfloat16))
-                  for _ in range(layers)]
-        q = torch.randn((batch, hq, dqk), generator=gen, device="cuda").to(torch.bfloat16)
-        bt_d = torch.from_numpy(bt).cuda()
-        lens_d = torch.from_numpy(lens).cuda()
-        qlens_d = torch.ones(batch, dtype=torch.int32, device="cuda")
-        out = torch.empty((batch, hq, dv), dtype=torch.bfloat16, device="cuda")
-        d = B.AttnDesc(batch=batch, num_q_heads=hq, num_kv_heads=hkv, head_dim_qk=dqk, head_dim_v=dv,
-                       page_size=P, num_pages=num_pages, block_table_stride=stride,
-                       max_seq_len=int(lens.max()), max_q_len=1, total_q=batch, kv_dtype=B.KV_BF16,
-                       force_num_splits=0)
-        nbytes = B.diffkv_attn_workspace_bytes(d, B.ENTRIES["decode"])
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
-        calls = [B.prepared_call("diffkv_attn_decode", d, q, k, v, bt_d, lens_d, qlens_d, 0, None, 1.0, 1.0,
-                                 1.0 / math.sqrt(dqk), out, None, None, ws, nbytes, stream)
-                 for k, v in caches]
-        total_ms, _, kern = time_calls(calls, steps, warmup, events, stream)
-        if not bool(torch.isfinite(out.float()).all()):
-            raise RuntimeError(f"decode sweep at {L0}: non-finite output")
-        kv_bytes = int(lens.astype(np.int64).sum()) * hkv * (dqk + dv) * 2
-        ms = sum(kern) / len(kern)
-        rows.append({"context_lo": int(L0), "kv_bytes": kv_bytes, "kernel_ms": round(ms, 5),
-                     "step_ms": round(total_ms / steps, 5),
-                     "kernel_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
-                     "frac": round(kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "layers": layers})
-        del caches, calls, ws, out
+        lens = rng.integers(L0, L0 + L0 // 8 + 1, size=32).astype(np.int32)
+        calls, out, kv_bytes, layers = _random_paged_call(lens, 1, rng, gen, stream, target_bytes, shuffle)
+        row = _sweep_point(calls, out, kv_bytes, layers, steps, warmup, events, stream, f"decode sweep at {L0}")
+        rows.append({"context_lo": int(L0), **row})
+        del calls, out
         torch.cuda.empty_cache()
     x = np.array([r["kv_bytes"] for r in rows], dtype=np.float64)
     y = np.array([r["kernel_ms"] * 1e-3 for r in rows], dtype=np.float64)
@@ -657,6 +706,7 @@ def main():
         print(f"[bench] {name}: generating and measuring", file=sys.stderr, flush=True)
         res = (measure_kv_write(name, args.steps, args.warmup, events) if name in KV_WRITE_OF
                else measure_decode_sweep(args.steps, args.warmup, events) if name == "decode_sweep"
+               else measure_verify_sweep(args.steps, args.warmup, events) if name == "verify_sweep"
                else measure_context_split(args.steps, args.warmup, events))
         print(json.dumps({"workload": name, "steps": args.steps, "warmup": args.warmup,
                           "kernel_source_sha": sha, **res}), flush=True)
@@ -710,6 +760,9 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] decode_sweep: generating and measuring", file=sys.stderr, flush=True)
         extra["decode_sweep"] = measure_decode_sweep(args.extra_steps, 5, events)
+        torch.cuda.empty_cache()
+        print("[bench] verify_sweep: generating and measuring", file=sys.stderr, flush=True)
+        extra["verify_sweep"] = measure_verify_sweep(args.extra_steps, 5, events)
         torch.cuda.empty_cache()
         result["extra"] = extra
     if args.copy_calibration:

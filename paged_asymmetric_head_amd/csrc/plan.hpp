@@ -80,14 +80,17 @@ template <bool FP8> constexpr int kSplitStages = FP8 ? DIFFKV_FP8_STAGES : DIFFK
 constexpr int kSplitWavesPerEu = DIFFKV_SPLIT_WAVES_PER_EU;
 constexpr int kSplitSlotsPerCu = DIFFKV_SPLIT_SLOTS_PER_CU;
 // Workgroups of 64 query rows (4 row tiles: a verify block at GQA 8 or
-// more) over a bf16 cache plan one chunk per CU instead: each workgroup
-// then has every SIMD to itself for its four times larger products, and the
-// fewer, longer chunks halve the partials the merge reads (verify at
-// 40K-50K tokens: 29.8 vs 30.5 us for the split kernel, 34.7 vs 35.7 us for
-// the call).  FP8 caches keep two: the widening adds VALU work per tile
-// that a second workgroup hides (the split part of a mixed FP8 batch took
-// 148 instead of 121 us with one).
+// more) over a bf16 cache plan one chunk per CU instead while those chunks
+// stay short (host bound: at most kSlots64MaxTilesPerCu tiles each): each
+// workgroup then has every SIMD to itself for its four times larger
+// products, and the fewer chunks halve the partials the merge reads (4
+// verify blocks at 40K-50K tokens: the call 36.2 vs 38.1 us with two per
+// CU).  Longer work goes back to two per CU, which keeps twice the loads in
+// flight (32 such blocks: the kernel 173 vs 180 us).  FP8 caches keep two:
+// the widening adds VALU work per tile that a second workgroup hides (the
+// split part of a mixed FP8 batch took 148 instead of 121 us with one).
 constexpr int kSplitSlotsPerCu64 = DIFFKV_SPLIT_SLOTS_PER_CU_64;
+constexpr long long kSlots64MaxTilesPerCu = 16;
 // plan_split's wgs_per_cu for a launch: slots chosen from the row tiles and
 // the cache format.
 constexpr int kLaunchSlots = -1;
@@ -111,11 +114,14 @@ inline SplitPlan plan_split(const diffkv_attn_desc& d, int window,
   const long long rows_pair = (long long)d.max_q_len * G;
   p.row_tiles = split_row_tiles((int)(rows_pair < 64 ? rows_pair : 64));
   p.rows = 16 * p.row_tiles;
-  if (wgs_per_cu == kLaunchSlots)
-    wgs_per_cu = p.row_tiles == 4 && d.kv_dtype == DIFFKV_KV_BF16 ? kSplitSlotsPerCu64 : kSplitSlotsPerCu;
   p.n_qtiles = ceil_div(rows_pair, p.rows);
   const long long pairs = (long long)d.batch * p.n_qtiles;
   const long long max_tiles = ceil_div(max_keys_bound(d, window), kTileKeys) + 1;
+  if (wgs_per_cu == kLaunchSlots)   // bound on the tiles one CU's single chunk would hold
+    wgs_per_cu = p.row_tiles == 4 && d.kv_dtype == DIFFKV_KV_BF16 &&
+                         pairs * max_tiles * d.num_kv_heads <= (long long)kSlots64MaxTilesPerCu * kTargetCUs
+                     ? kSplitSlotsPerCu64
+                     : kSplitSlotsPerCu;
   const int per_head = kTargetCUs * wgs_per_cu / d.num_kv_heads;
   p.slots = per_head > 1 ? per_head : 1;
   if (d.force_num_splits > 0) {
