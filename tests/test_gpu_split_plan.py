@@ -57,3 +57,12 @@ def test_chunks_lengthened_to_fit_one_round(batch, seed, lo, hi, hq, hkv, page):
     inp = make_paged_inputs(405 + batch, seq_lens=lens, q_lens=1, num_q_heads=hq, num_kv_heads=hkv,
                             page_size=page, kv_dtype="bf16", sinks=True)
     check_call(DeviceInputs(inp), "decode", f"{batch} sequences, chunks fitted to one round")
+
+
+def test_verify_over_the_one_slot_bound():
+    """A bf16 verify batch (64-row tiles) whose host bound exceeds 16 tiles per
+    one-per-CU chunk, so the plan takes two workgroups per CU."""
+    lens = [int(x) for x in np.random.default_rng(406).integers(20000, 24000, size=12)]
+    inp = make_paged_inputs(407, seq_lens=lens, q_lens=8, num_q_heads=8, num_kv_heads=1,
+                            page_size=128, kv_dtype="bf16", sinks=False)
+    check_call(DeviceInputs(inp), "verify", "verify over the one-slot bound")
