@@ -114,9 +114,21 @@ hipError_t dispatch_split(const SplitArgs& a, int dqk, int rt, bool upage, dim3 
              : dispatch_split_dqk<FP8, kHeadDimQK>(a, rt, upage, grid, direct, count, st);
 }
 
-// Merge shape by the bound on chunks per pair: one wave with 16 loads when
-// that covers every chunk, else four waves with 32 loads each (128 chunks per
-// pass), of which a pair of at most 32 chunks uses one.
+// Merge shape by the chunks a pair is expected to have: one wave with 16
+// loads per pass when that is at most 16, else four waves with 32 loads each
+// (128 chunks per pass), of which a pair of at most 32 chunks uses one.
+// Either shape takes any chunk count (more passes).  The expectation is the
+// plan's slots over its pairs (the balanced plan gives near-uniform batches
+// about that many each; decode at 8K tokens: 16, where the worst-case bound
+// is 37 and picked the four-wave shape, 1 us slower per call); forced splits
+// are exact.
+int expected_chunks_per_pair(const SplitPlan& plan, const diffkv_attn_desc& d) {
+  if (d.force_num_splits > 0) return plan.max_chunks;
+  const long long pairs = (long long)d.batch * plan.n_qtiles;
+  const long long e = (plan.slots + pairs - 1) / pairs;
+  return (int)(e < plan.max_chunks ? e : plan.max_chunks);
+}
+
 template <int ROWS>
 const void* merge_kernel_for(int splits, int& threads) {
   if (splits <= 16) { threads = 64; return reinterpret_cast<const void*>(&split_merge_kernel<ROWS, 1, 16>); }
@@ -252,7 +264,7 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
             : dispatch_split<false>(sa, d->head_dim_qk, plan.row_tiles, upage, grid, plan.direct, count,
                                     stream);
     if (e == hipSuccess && !plan.direct)
-      e = launch_merge(sa, plan.rows, plan.max_chunks,
+      e = launch_merge(sa, plan.rows, expected_chunks_per_pair(plan, *d),
                        dim3(sd.max_q_len * G, d->batch * d->num_kv_heads), stream);
     if (e != hipSuccess) return DIFFKV_HIP_ERROR;
   }
