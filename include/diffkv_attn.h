@@ -259,9 +259,13 @@ size_t diffkv_attn_workspace_bytes(const diffkv_attn_desc* desc, int entry);
 /* Synchronous check of a descriptor for an entry; host only, no HIP call. */
 int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry);
 
-/* Number of key-axis splits the entry launches for this descriptor and
- * window (1 for prefill; for mixed, the split count of its split-KV part;
- * 0 for an invalid descriptor).  Host only. */
+/* Upper bound on the key-axis chunks one (sequence, query tile) pair is cut
+ * into for this descriptor and window (the kernels cut the keys on the
+ * device from the actual lengths, in chunks that fit one resident round of
+ * workgroups; this host-side bound sizes the merge): 1 when the keys are
+ * not split (prefill, short windows), force_num_splits when that is set;
+ * for mixed, the bound of its split-KV part; 0 for an invalid descriptor.
+ * Host only. */
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window);
 
 /* Profiling hook.  Arms two caller-created HIP events for the next
