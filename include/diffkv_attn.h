@@ -273,8 +273,9 @@ int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t wind
  * thread: that call's first main kernel (not the split merge; for mixed, the
  * split-KV kernel) is dispatched with them as its
  * start and stop events (hipExtLaunchKernel), so hipEventElapsedTime(start,
- * stop) is that kernel's execution time.  The hook disarms after one call;
- * passing two NULLs disarms it.  Returns DIFFKV_INVALID_ARGUMENT if exactly
+ * stop) is that kernel's execution time.  The hook disarms after one call,
+ * also when that call returns an error before launching (the events are
+ * then left as they were); passing two NULLs disarms it.  Returns DIFFKV_INVALID_ARGUMENT if exactly
  * one event is NULL. */
 int diffkv_attn_profile_next_call(hipEvent_t start, hipEvent_t stop);
 

@@ -24,6 +24,13 @@ namespace {
 thread_local hipEvent_t g_profile_start = nullptr;
 thread_local hipEvent_t g_profile_stop = nullptr;
 
+// Disarms the profiling events when an entry point returns, so a call that
+// fails before its launch still consumes them (launch_main disarms them when
+// it dispatches with them).
+struct ProfileDisarm {
+  ~ProfileDisarm() { g_profile_start = g_profile_stop = nullptr; }
+};
+
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int ilog2(int x) {
@@ -192,6 +199,7 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
               float v_scale, float softmax_scale, void* out, float* lse_out, int32_t* count_out,
               void* workspace, size_t workspace_bytes, hipStream_t stream,
               const PartialMode& pm = PartialMode()) {
+  const ProfileDisarm disarm;
   const int st = validate_desc(d, entry);
   if (st != DIFFKV_OK) return st;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !(out || pm.part_out))
@@ -288,6 +296,7 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
 int run_kv_write(const diffkv_attn_desc* d, const void* k_new, const void* v_new, void* k_cache,
                  void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                  const int32_t* q_lens, float k_scale, float v_scale, hipStream_t stream) {
+  const ProfileDisarm disarm;
   const int st = validate_desc(d, DIFFKV_ENTRY_PREFILL);
   if (st != DIFFKV_OK) return st;
   if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !seq_lens)
@@ -374,6 +383,7 @@ int diffkv_attn_partial(const diffkv_attn_desc* desc, const void* q, const void*
                         int32_t window, float k_scale, float v_scale, float softmax_scale,
                         float* out_part, float* lse_part, int32_t* count_out, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
+  const ProfileDisarm disarm;
   if (out_part == nullptr || lse_part == nullptr) return DIFFKV_INVALID_ARGUMENT;
   PartialMode pm;
   pm.key_lo = key_lo;
@@ -387,6 +397,7 @@ int diffkv_attn_partial(const diffkv_attn_desc* desc, const void* q, const void*
 int diffkv_attn_combine(int32_t num_parts, int32_t rows, int32_t num_q_heads,
                         const float* out_parts, const float* lse_parts, const float* sinks,
                         void* out, float* lse_out, hipStream_t stream) {
+  const ProfileDisarm disarm;
   if (num_parts < 1 || rows < 1 || num_q_heads < 1 || rows % num_q_heads != 0)
     return DIFFKV_INVALID_ARGUMENT;
   if (num_parts > kMaxCombineParts) return DIFFKV_UNSUPPORTED;

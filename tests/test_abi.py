@@ -197,3 +197,12 @@ def test_stream_reference_library_loads_and_rejects_bad_arguments():
     assert fn(16, 17, 16, 1, 4, None) == 1              # not a multiple of 16 bytes
     assert fn(8, 16, 16, 1, 4, None) == 1               # misaligned source
     assert fn(16, 16, 16, 1, 5, None) == 1              # unsupported loads per thread
+
+
+def test_profile_hook_rejects_one_null_event(lib):
+    """Arming takes both events or neither (host only: the handles are only
+    stored, never used, and the last call disarms)."""
+    fake = 256
+    assert lib.diffkv_attn_profile_next_call(fake, None) == B.INVALID_ARGUMENT
+    assert lib.diffkv_attn_profile_next_call(None, fake) == B.INVALID_ARGUMENT
+    assert lib.diffkv_attn_profile_next_call(None, None) == B.OK

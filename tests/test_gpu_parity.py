@@ -160,9 +160,10 @@ def test_fp8_values_pass_through_exactly(entry):
 @pytest.mark.parametrize("q_len,hq,splits", [(1, 8, 0), (1, 8, 9), (4, 8, 5), (8, 8, 40)])
 def test_workspace_reuse_across_calls(q_len, hq, splits):
     """One workspace, several calls with different sequence lengths inside the
-    same descriptor bounds: the split partials and the arrival counters the
-    last split uses to merge must leave the workspace ready for the next call
-    (both the fused-merge and the merge-kernel paths)."""
+    same descriptor bounds: the partial rows and per-pair chunk records one
+    call leaves in the workspace must not reach the next call's output (every
+    call records its own chunk ranges; pairs of one chunk write their rows
+    directly and the merge skips them)."""
     from paged_asymmetric_head_amd import binding as B
     entry = "decode" if q_len == 1 else "verify"
     lens = [[3000, 2500, 700], [2999, 64, 3001], [1, 3001, 1500]]
