@@ -213,6 +213,13 @@ void prefill_attn_kernel(const SplitArgs a) {
     // two transposing reads.  The row sums of this tile's (bf16) P come from
     // the matrix cores too: an all-ones V^T tile gives sum_k P[row][k] in
     // every element, across all four lane groups, with no shuffles.
+    // The products and the next tile's widening store run at raised wave
+    // priority, the softmax at the base level: of the two waves on a SIMD,
+    // one entering its products issues ahead of the other's softmax, so the
+    // pair drifts out of lock step and one wave's softmax runs beside the
+    // other's matrix work (2.125 -> 2.084 ms on the chunked-prefill
+    // workload, bit-identical outputs).
+    __builtin_amdgcn_s_setprio(1);
     f32x4 psum[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) psum[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -228,6 +235,7 @@ void prefill_attn_kernel(const SplitArgs a) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) psum[rt] = mfma_16x16x32(kOnesBf16x8, pt[rt][c], psum[rt]);
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) l[rt] = __builtin_fmaf(l[rt], alpha[rt], psum[rt][0]);
   };
@@ -245,7 +253,9 @@ void prefill_attn_kernel(const SplitArgs a) {
       // Widen tile t + 1 into the other buffer (its last readers passed the
       // barrier that ended the previous tile), then start loading t + 1 + NS.
       const int j = (i + 1) % NS;   // a constant once the loop is unrolled
+      __builtin_amdgcn_s_setprio(1);
       io.store(st[j], nxt, nxt + kKLdsElems<DQK>);
+      __builtin_amdgcn_s_setprio(0);
       io.fetch_data(t + 1 + NS, pg[j], st[j]);
       io.fetch_pages(t + 1 + 2 * NS, pg[j]);
       __syncthreads();
