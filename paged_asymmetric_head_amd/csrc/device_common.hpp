@@ -100,27 +100,30 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 
-// A register copy the compiler cannot look through.
-__device__ __forceinline__ uint32_t opaque_copy(uint32_t x) {
-  uint32_t y;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
-  return y;
+// v_max_f32 of two raw registers.  Written out because fmaxf here costs
+// three more instructions: the compiler cannot tell that the row-swap
+// results below are canonical floats, so it re-canonicalises both operands
+// (v_max x, x) before the max.  The operands are scores, -inf or magnitudes,
+// never NaN, so no quieting is needed.  Also opaque to the compiler: with
+// fmaxf on the swap results this compiler (ROCm 7.2 clang) once replaced
+// the second result by the first and the max silently disappeared.
+__device__ __forceinline__ float max_raw(uint32_t a, uint32_t b) {
+  float r;
+  asm volatile("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 // Max over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48) on
 // the VALU, with gfx950's row swaps instead of LDS permutes.  Called with
 // both operands equal, v_permlane16_swap returns the values of the even and
 // the odd row of each row pair, v_permlane32_swap those of the low and the
-// high half-wave.  The second result goes through opaque_copy: without it
-// this compiler (ROCm 7.2 clang) replaces the second result by the first
-// once it is reinterpreted as a float, and the max silently disappears.
+// high half-wave.
 __device__ __forceinline__ float max_over_lane_groups(float v) {
   const uint32_t x = __builtin_bit_cast(uint32_t, v);
   const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  v = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, opaque_copy(a[1])));
-  const uint32_t y = __builtin_bit_cast(uint32_t, v);
+  const uint32_t y = __builtin_bit_cast(uint32_t, max_raw(a[0], a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, opaque_copy(b[1])));
+  return max_raw(b[0], b[1]);
 }
 
 __device__ __forceinline__ int wave_sum_int(int v) {
