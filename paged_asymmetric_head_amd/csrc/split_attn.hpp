@@ -449,8 +449,14 @@ void split_attn_kernel(const SplitArgs a) {
       if constexpr (!WAVE_LOCAL) __syncthreads();
       io.store(st[i], k_lds, v_lds);
       if constexpr (!WAVE_LOCAL) __syncthreads();
+      // With wave-local tiles a wave issues its next loads at raised
+      // priority, ahead of the other waves' products on its SIMD, so the
+      // next tile is requested as soon as this one is in LDS (batched decode
+      // 37.5 -> 36.7 us; the shared 32- and 64-row tiles gain nothing).
+      if constexpr (WAVE_LOCAL) __builtin_amdgcn_s_setprio(1);
       io.fetch_data(t + i + NS, pg[i], st[i]);
       io.fetch_pages(t + i + 2 * NS, pg[i]);
+      if constexpr (WAVE_LOCAL) __builtin_amdgcn_s_setprio(0);
       if (t + i < t_end) compute_tile(t + i);
     }
   }
