@@ -93,24 +93,40 @@ def _piece_edges(j0, j1, split, page_size):
     return np.round(np.linspace(j0, j1 + 1, k + 1)).astype(np.int64)
 
 
-def _direct(x, V, s_h):
+def _sum_visible(e, vis, V):
+    """sum_j e[a, g, j] * V[j, :] over the keys j that row a sees (vis[a, j]).
+
+    A key a row does not see adds nothing, not even 0 * NaN: value entries
+    that are not finite are summed over the visible keys alone.
+    """
+    finite = np.isfinite(V)
+    o = np.matmul(e, np.where(finite, V, 0.0))
+    for d in np.flatnonzero(~finite.all(axis=0)):
+        with np.errstate(invalid="ignore"):
+            o[..., d] = np.where(vis[:, None, :], e * V[None, None, :, d], 0.0).sum(axis=2)
+    return o
+
+
+def _direct(x, vis, V, s_h):
     """The definition itself: one max, one denominator, one weighted sum.
 
-    x [ni, G, nj] scaled scores with invisible keys at -inf; V [nj, Dv];
-    s_h [G] sink logits or None.
+    x [ni, G, nj] scaled scores with invisible keys at -inf; vis [ni, nj] the
+    visible keys; V [nj, Dv]; s_h [G] sink logits or None.  A NaN score of a
+    visible key stays NaN and reaches the output, as in the definition.
     """
-    m = x.max(axis=2)                                                # [ni, G]
+    m = x.max(axis=2)                                                # [ni, G]; NaN propagates
     if s_h is not None:
         m = np.maximum(m, s_h[None, :])
-    e = np.where(np.isfinite(x), np.exp(x - m[:, :, None]), 0.0)    # exp(-inf) -> 0
+    with np.errstate(invalid="ignore"):
+        e = np.where(vis[:, None, :], np.exp(x - m[:, :, None]), 0.0)
     key_sum = e.sum(axis=2)
     den = key_sum + (0.0 if s_h is None else np.exp(s_h[None, :] - m))
-    o = np.matmul(e, V) / den[:, :, None]
+    o = _sum_visible(e, vis, V) / den[:, :, None]
     with np.errstate(divide="ignore"):
         return o, m + np.log(key_sum)
 
 
-def _pieces_merged(x, V, s_h, edges):
+def _pieces_merged(x, vis, V, s_h, edges):
     """Split-KV evaluation: per piece (max, sum, normalised output), merged by
     log-sum-exp with the sink joining the merged denominator."""
     piece_lse, piece_out = [], []
@@ -118,20 +134,23 @@ def _pieces_merged(x, V, s_h, edges):
         if e1 <= e0:
             continue
         xs = x[:, :, e0:e1]
+        vs = vis[:, e0:e1]
         m = xs.max(axis=2)                                            # -inf if none visible
-        m_safe = np.where(np.isfinite(m), m, 0.0)
-        w = np.where(np.isfinite(xs), np.exp(xs - m_safe[:, :, None]), 0.0)
+        m_safe = np.where(m == -np.inf, 0.0, m)
+        with np.errstate(invalid="ignore"):
+            w = np.where(vs[:, None, :], np.exp(xs - m_safe[:, :, None]), 0.0)
         l = w.sum(axis=2)
-        o = np.matmul(w, V[e0:e1])
+        o = _sum_visible(w, vs, V[e0:e1])
         with np.errstate(invalid="ignore", divide="ignore"):
-            piece_out.append(np.where(l[:, :, None] > 0, o / l[:, :, None], 0.0))
-            piece_lse.append(np.where(l > 0, m_safe + np.log(l), -np.inf))
+            piece_out.append(np.where(l[:, :, None] == 0, 0.0, o / l[:, :, None]))
+            piece_lse.append(np.where(l == 0, -np.inf, m_safe + np.log(l)))
     pl = np.stack(piece_lse)                                          # [S, ni, G]
     po = np.stack(piece_out)                                          # [S, ni, G, Dv]
     M = pl.max(axis=0)
     if s_h is not None:
         M = np.maximum(M, s_h[None, :])
-    wts = np.where(np.isfinite(pl), np.exp(pl - M[None]), 0.0)
+    with np.errstate(invalid="ignore"):
+        wts = np.where(pl == -np.inf, 0.0, np.exp(pl - M[None]))      # empty pieces only
     key_sum = wts.sum(axis=0)
     den = key_sum + (0.0 if s_h is None else np.exp(s_h[None, :] - M))
     o = (wts[..., None] * po).sum(axis=0) / den[..., None]
@@ -234,9 +253,9 @@ def paged_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens=None, *,
                 x = np.where(vis[:, None, :], x, -np.inf)
 
                 if split is None:
-                    o, row_lse = _direct(x, V, s_h)
+                    o, row_lse = _direct(x, vis, V, s_h)
                 else:
-                    o, row_lse = _pieces_merged(x, V, s_h, edges)
+                    o, row_lse = _pieces_merged(x, vis, V, s_h, edges)
 
                 cnt = vis.sum(axis=1)
                 for a, t in enumerate(li):
@@ -280,7 +299,8 @@ def combine_partials(outs, lses, sinks=None):
     M = lses.max(axis=0)
     if sinks is not None:
         M = np.maximum(M, np.asarray(sinks, dtype=np.float64)[None, :])
-    w = np.where(np.isfinite(lses), np.exp(lses - M[None]), 0.0)
+    with np.errstate(invalid="ignore"):
+        w = np.where(lses == -np.inf, 0.0, np.exp(lses - M[None]))   # empty parts only
     key_sum = w.sum(axis=0)
     den = key_sum + (0.0 if sinks is None else np.exp(np.asarray(sinks, dtype=np.float64)[None, :] - M))
     out = (w[..., None] * outs).sum(axis=0) / den[..., None]

@@ -55,8 +55,11 @@ def paged_kv_write(k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_lens
                 kc[page, slot] = k_new[r0 + i]
                 vc[page, slot] = v_new[r0 + i]
             else:
-                k = decode_bf16(k_new[r0 + i]).astype(np.float32) / ks
-                v = decode_bf16(v_new[r0 + i]).astype(np.float32) / vs
+                # A quotient may overflow to +-inf (a large value over a small
+                # scale); the encoder clamps it to +-448.
+                with np.errstate(over="ignore"):
+                    k = decode_bf16(k_new[r0 + i]).astype(np.float32) / ks
+                    v = decode_bf16(v_new[r0 + i]).astype(np.float32) / vs
                 kc[page, slot] = encode_e4m3fn(k)
                 vc[page, slot] = encode_e4m3fn(v)
         r0 += n

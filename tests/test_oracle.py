@@ -279,6 +279,43 @@ def test_nan_tails_never_reach_the_output():
     assert np.array_equal(res.out, ref.out)
 
 
+@pytest.mark.parametrize("which,split", [("k", None), ("v", None), ("k", 3), ("v", "page")])
+def test_nan_in_a_visible_key_propagates(which, split):
+    """The definition sums over every visible key, so a NaN in a visible K or V
+    row makes every output row that sees it NaN (all query heads of that KV
+    head), while rows that do not see it (earlier tokens of the causal block,
+    other KV heads, other sequences) stay finite.  Only masked keys may be
+    dropped; an oracle that zeroed every non-finite score would hide a kernel
+    that silently skips NaN keys."""
+    inp = make_paged_inputs(31, seq_lens=[40, 25], q_lens=[4, 2], num_q_heads=4, num_kv_heads=2,
+                            page_size=8, kv_dtype="bf16", sinks=True)
+    L, n, P = 40, 4, 8
+    j = L - n + 2                                   # key of token 2: seen by tokens 2 and 3 only
+    page, slot = inp.block_table[0, j // P], j % P
+    cache = inp.k_cache if which == "k" else inp.v_cache
+    cache[page, slot, 1, 5] = 0x7FC0                # NaN in KV head 1's row
+    res = run(inp, split=split)
+    bad = np.isnan(res.out).any(axis=2)             # [total_q, Hq]
+    want = np.zeros_like(bad)
+    want[2:4, 2:4] = True                           # tokens 2, 3 of sequence 0; heads of KV head 1
+    assert np.array_equal(bad, want)
+    if which == "v":                                # NaN in one V dim: only that dim
+        assert np.isnan(res.out[2:4, 2:4, 5]).all()
+        assert np.isfinite(np.delete(res.out[2:4, 2:4], 5, axis=2)).all()
+    else:
+        assert np.isnan(res.out[2:4, 2:4]).all() and np.isnan(res.lse[2:4, 2:4]).all()
+
+
+def test_nan_partial_propagates_through_combine():
+    from oracle import combine_partials
+    outs = np.zeros((3, 2, 2, 4))
+    lses = np.array([[[0.5, -np.inf], [1.0, 2.0]], [[np.nan, 0.0], [0.0, 0.0]],
+                     [[-np.inf, -np.inf], [0.3, 0.1]]])
+    out, lse = combine_partials(outs, lses, sinks=np.array([0.0, 1.0]))
+    assert np.isnan(out[0, 0]).all() and np.isnan(lse[0, 0])
+    assert np.isfinite(out[[0, 1, 1], [1, 0, 1]]).all()
+
+
 def test_oracle_rejects_unreadable_visible_page():
     inp = make_paged_inputs(3, seq_lens=[20], q_lens=1, num_q_heads=1, num_kv_heads=1,
                             page_size=4, kv_dtype="bf16")
