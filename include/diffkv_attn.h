@@ -118,6 +118,11 @@ typedef struct diffkv_attn_desc {
  * no reference after returning, never allocates, frees or synchronises, and
  * never reads device data on the host.  out must not alias an input.
  *
+ * Thread safety: every call is re-entrant.  The library's only state is the
+ * compute-unit count of each device (filled once per device under
+ * std::call_once) and the one-call profiling slot of each host thread
+ * (diffkv_attn_profile_next_call, thread_local, empty unless armed).
+ *
  * Preconditions on device data (undefined behaviour if broken):
  *   1 <= q_lens[b] <= seq_lens[b] <= max_seq_len, q_lens[b] <= max_q_len,
  *   sum(q_lens) == total_q, and every block-table entry that is read lies in
@@ -251,9 +256,13 @@ int diffkv_kv_write(const diffkv_attn_desc* desc, const void* k_new, const void*
                     const int32_t* seq_lens, const int32_t* q_lens, float k_scale, float v_scale,
                     hipStream_t stream);
 
-/* Bytes of workspace the entry needs for this descriptor (0 when none).
- * Host only; depends on the descriptor alone.  Returns 0 for an invalid
- * descriptor (check diffkv_attn_validate). */
+/* Bytes of workspace the entry needs for this descriptor (0 when none) on
+ * the current device.  Host only: depends on the descriptor and the device's
+ * compute-unit count (queried once per device and cached; 256, MI355X's
+ * count, when no device can be queried).  A call on a stream of another
+ * device with more compute units may need more (it then returns
+ * DIFFKV_WORKSPACE_TOO_SMALL).  Returns 0 for an invalid descriptor (check
+ * diffkv_attn_validate). */
 size_t diffkv_attn_workspace_bytes(const diffkv_attn_desc* desc, int entry);
 
 /* Synchronous check of a descriptor for an entry; host only, no HIP call. */
@@ -265,7 +274,7 @@ int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry);
  * workgroups; this host-side bound sizes the merge): 1 when the keys are
  * not split (prefill, short windows), force_num_splits when that is set;
  * for mixed, the bound of its split-KV part; 0 for an invalid descriptor.
- * Host only. */
+ * Host only; for the current device's compute-unit count. */
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window);
 
 /* Profiling hook.  Arms two caller-created HIP events for the next

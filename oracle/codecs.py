@@ -26,9 +26,8 @@ def decode_bf16(bits):
         return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
-def decode_e4m3fn(codes):
-    """OCP E4M3FN codes (uint8 array) -> float64, exact; 0x7F and 0xFF give NaN."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+def _e4m3fn_value(c):
+    """The value of each E4M3FN code in c (int64 array) from the format's fields."""
     sign = np.where((c >> 7) & 1, -1.0, 1.0)
     e = (c >> 3) & 0xF
     m = (c & 0x7).astype(np.float64)
@@ -37,6 +36,16 @@ def decode_e4m3fn(codes):
     mag = np.where(e > 0, normal, subnormal)
     out = sign * mag
     return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+# All 256 codes' values, evaluated once from the fields above: decoding a
+# large cache is then one table lookup per code (same values).
+_E4M3_VALUES = _e4m3fn_value(np.arange(256, dtype=np.int64))
+
+
+def decode_e4m3fn(codes):
+    """OCP E4M3FN codes (uint8 array) -> float64, exact; 0x7F and 0xFF give NaN."""
+    return _E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
 
 
 # The 127 non-negative finite E4M3FN values, in code order (ascending).

@@ -8,9 +8,11 @@
 #include <hip/hip_ext.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "diffkv_attn.h"
 #include "plan.hpp"
+#include "validate.hpp"
 #include "split_attn.hpp"
 #include "prefill_attn.hpp"
 #include "kv_write.hpp"
@@ -24,48 +26,43 @@ namespace {
 thread_local hipEvent_t g_profile_start = nullptr;
 thread_local hipEvent_t g_profile_stop = nullptr;
 
+// Compute units per device, queried once per device (the planner's one
+// resident round of workgroups is sized from it).  kDefaultCUs when the
+// device cannot be queried (no GPU, or an ordinal past kMaxDevices).
+constexpr int kMaxDevices = 64;
+std::once_flag g_cu_once[kMaxDevices];
+int g_cu_count[kMaxDevices];
+
+int device_cu_count(int device) {
+  if (device < 0 || device >= kMaxDevices) return kDefaultCUs;
+  std::call_once(g_cu_once[device], [device] {
+    int n = 0;
+    const hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device);
+    g_cu_count[device] = e == hipSuccess && n > 0 ? n : kDefaultCUs;
+  });
+  return g_cu_count[device];
+}
+
+// CUs of the device a stream belongs to (the current device for the null
+// stream, and for workspace sizing, which has no stream).
+int stream_cu_count(hipStream_t stream) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) == hipSuccess) return device_cu_count(dev);
+  }
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();                 // leave no sticky error for the caller
+    return kDefaultCUs;
+  }
+  return device_cu_count(dev);
+}
+
 // Disarms the profiling events when an entry point returns, so a call that
 // fails before its launch still consumes them (launch_main disarms them when
 // it dispatches with them).
 struct ProfileDisarm {
   ~ProfileDisarm() { g_profile_start = g_profile_stop = nullptr; }
 };
-
-bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
-
-int ilog2(int x) {
-  int r = 0;
-  while ((1 << r) < x) ++r;
-  return r;
-}
-
-int validate_desc(const diffkv_attn_desc* d, int entry) {
-  if (d == nullptr) return DIFFKV_INVALID_ARGUMENT;
-  if (entry < DIFFKV_ENTRY_DECODE || entry > DIFFKV_ENTRY_MIXED) return DIFFKV_INVALID_ARGUMENT;
-  if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1) return DIFFKV_INVALID_ARGUMENT;
-  if (d->num_q_heads % d->num_kv_heads != 0) return DIFFKV_INVALID_ARGUMENT;
-  if ((d->head_dim_qk != kHeadDimQK && d->head_dim_qk != kHeadDimQKSym) || d->head_dim_v != kHeadDimV)
-    return DIFFKV_UNSUPPORTED;
-  if (!is_pow2(d->page_size) || d->page_size > 256) return DIFFKV_UNSUPPORTED;
-  if (d->kv_dtype != DIFFKV_KV_BF16 && d->kv_dtype != DIFFKV_KV_FP8_E4M3) return DIFFKV_UNSUPPORTED;
-  if (d->num_pages < 1 || d->max_seq_len < 1 || d->max_q_len < 1 || d->total_q < 1)
-    return DIFFKV_INVALID_ARGUMENT;
-  if (d->max_q_len > d->max_seq_len) return DIFFKV_INVALID_ARGUMENT;
-  if ((long long)d->block_table_stride * d->page_size < d->max_seq_len) return DIFFKV_INVALID_ARGUMENT;
-  if (d->total_q < d->batch || (long long)d->total_q > (long long)d->batch * d->max_q_len)
-    return DIFFKV_INVALID_ARGUMENT;
-  if (d->force_num_splits < 0) return DIFFKV_INVALID_ARGUMENT;
-  if (entry == DIFFKV_ENTRY_DECODE && d->max_q_len != 1) return DIFFKV_INVALID_ARGUMENT;
-  if (entry == DIFFKV_ENTRY_VERIFY && d->max_q_len > 16) return DIFFKV_INVALID_ARGUMENT;
-  // Launch-shape limits.
-  if ((long long)d->batch * d->num_kv_heads > kMaxGridYZ) return DIFFKV_UNSUPPORTED;
-  if (entry != DIFFKV_ENTRY_PREFILL) {
-    const SplitPlan p = plan_split(split_part_desc(*d, entry), 0);
-    if (p.grid_x > INT32_MAX) return DIFFKV_UNSUPPORTED;
-  }
-  if ((long long)d->total_q * d->num_q_heads > (1LL << 31) / kHeadDimQK) return DIFFKV_UNSUPPORTED;
-  return DIFFKV_OK;
-}
 
 // Launches the main attention kernel of a call.  When profiling events are
 // armed, the dispatch itself stamps them (hipExtLaunchKernel), so their
@@ -249,7 +246,7 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
   // Split-KV part: decode and verify, and a mixed call's short sequences.
   if (entry != DIFFKV_ENTRY_PREFILL) {
     const diffkv_attn_desc sd = split_part_desc(*d, entry);
-    const SplitPlan plan = plan_split(sd, window, kLaunchSlots);
+    const SplitPlan plan = plan_split(sd, window, stream_cu_count(stream), kLaunchSlots);
     if (!plan.direct && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
       return DIFFKV_WORKSPACE_TOO_SMALL;
     SplitArgs sa = a;
@@ -424,7 +421,7 @@ int diffkv_attn_mixed(const diffkv_attn_desc* desc, const void* q, const void* k
 size_t diffkv_attn_workspace_bytes(const diffkv_attn_desc* desc, int entry) {
   if (validate_desc(desc, entry) != DIFFKV_OK) return 0;
   if (entry == DIFFKV_ENTRY_PREFILL) return 0;
-  return plan_split(split_part_desc(*desc, entry), 0).workspace_bytes;
+  return plan_split(split_part_desc(*desc, entry), 0, stream_cu_count(nullptr)).workspace_bytes;
 }
 
 int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry) {
@@ -434,7 +431,8 @@ int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry) {
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window) {
   if (validate_desc(desc, entry) != DIFFKV_OK) return 0;
   if (entry == DIFFKV_ENTRY_PREFILL) return 1;
-  return plan_split(split_part_desc(*desc, entry), window, kLaunchSlots).max_chunks;
+  return plan_split(split_part_desc(*desc, entry), window, stream_cu_count(nullptr), kLaunchSlots)
+      .max_chunks;
 }
 
 int diffkv_attn_profile_next_call(hipEvent_t start, hipEvent_t stop) {

@@ -17,7 +17,9 @@ constexpr int kHeadDimQK = 192;      // key head dim of the asymmetric layers
 constexpr int kHeadDimQKSym = 128;   // key head dim of symmetric (128/128) heads
 constexpr int kHeadDimV = 128;
 constexpr int kTileKeys = 64;        // keys per split-kernel tile
-constexpr int kTargetCUs = 256;      // MI355X: 256 compute units in 8 XCDs
+constexpr int kDefaultCUs = 256;     // MI355X: 256 compute units in 8 XCDs (the count used
+                                     // when no device can be queried)
+constexpr int kMaxCUs = 1024;        // largest CU count a descriptor is validated for
 constexpr int kMaxGridYZ = 65535;
 
 // Query rows per split-kernel workgroup: 16 * row_tiles, row_tiles in {1,2,4}.
@@ -95,20 +97,21 @@ constexpr long long kSlots64MaxTilesPerCu = 16;
 // the cache format.
 constexpr int kLaunchSlots = -1;
 
-// Split plan from host bounds.  The kernels cut the keys on the device
-// (balanced chunks of C = max(kMinTilesPerSplit, ceil(T / slots)) tiles, T
-// the key tiles of the whole call), so the host fixes only the bounds: slots
-// = one resident round of workgroups over the 256 CUs per KV head (a second
-// round would pay the start-up chain seq_lens -> block table -> data again),
-// at most slots + pairs chunks per KV head (each pair's last chunk may be
-// short), and no split at all when no pair can hold more than
-// kMinTilesPerSplit tiles (short windows).  A larger wgs_per_cu only grows
-// the bounds, so the workspace sized for 4 workgroups per CU covers every
-// launch.
+// Split plan from host bounds and the device's CU count (a pure function of
+// both).  The kernels cut the keys on the device (balanced chunks of
+// C = max(kMinTilesPerSplit, ceil(T / slots)) tiles, T the key tiles of the
+// whole call), so the host fixes only the bounds: slots = one resident round
+// of workgroups over the num_cus CUs per KV head (a second round would pay
+// the start-up chain seq_lens -> block table -> data again), at most
+// slots + pairs chunks per KV head (each pair's last chunk may be short), and
+// no split at all when no pair can hold more than kMinTilesPerSplit tiles
+// (short windows).  A larger wgs_per_cu only grows the bounds, so the
+// workspace sized for 4 workgroups per CU covers every launch on that device.
 constexpr int kMinTilesPerSplit = DIFFKV_MIN_TILES_PER_SPLIT;
+constexpr int kWorkspaceWgsPerCu = kSplitSlotsPerCu > 4 ? kSplitSlotsPerCu : 4;
 
-inline SplitPlan plan_split(const diffkv_attn_desc& d, int window,
-                            int wgs_per_cu = kSplitSlotsPerCu > 4 ? kSplitSlotsPerCu : 4) {
+inline SplitPlan plan_split(const diffkv_attn_desc& d, int window, int num_cus,
+                            int wgs_per_cu = kWorkspaceWgsPerCu) {
   SplitPlan p;
   const int G = d.num_q_heads / d.num_kv_heads;
   const long long rows_pair = (long long)d.max_q_len * G;
@@ -119,11 +122,11 @@ inline SplitPlan plan_split(const diffkv_attn_desc& d, int window,
   const long long max_tiles = ceil_div(max_keys_bound(d, window), kTileKeys) + 1;
   if (wgs_per_cu == kLaunchSlots)   // bound on the tiles one CU's single chunk would hold
     wgs_per_cu = p.row_tiles == 4 && d.kv_dtype == DIFFKV_KV_BF16 &&
-                         pairs * max_tiles * d.num_kv_heads <= (long long)kSlots64MaxTilesPerCu * kTargetCUs
+                         pairs * max_tiles * d.num_kv_heads <= (long long)kSlots64MaxTilesPerCu * num_cus
                      ? kSplitSlotsPerCu64
                      : kSplitSlotsPerCu;
-  const int per_head = kTargetCUs * wgs_per_cu / d.num_kv_heads;
-  p.slots = per_head > 1 ? per_head : 1;
+  const long long per_head = (long long)num_cus * wgs_per_cu / d.num_kv_heads;
+  p.slots = per_head > 1 ? (int)per_head : 1;
   if (d.force_num_splits > 0) {
     p.direct = d.force_num_splits == 1;
     p.max_chunks = d.force_num_splits;

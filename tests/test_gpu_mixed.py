@@ -78,16 +78,13 @@ def test_mixed_matches_single_entries_bitwise():
             assert torch.equal(a[r0[s]:r0[s + 1]], b[r0[s]:r0[s + 1]]), s
 
 
-def test_mixed_batch_workload_sampled_rows():
+def test_mixed_batch_workload():
     """The full-size mixed step (a 4096-token chunk at 26K context, 4 verify
     blocks at 40K-50K, 32 decodes at 8K-9K; GQA 32/2, FP8, page 128): every
-    verify and decode row, and sampled rows of the chunk."""
+    row of the output against the oracle."""
     inp = workload("mixed_batch")
     dev = DeviceInputs(inp)
-    rng = np.random.default_rng(56)
-    chunk = np.concatenate([[0, 1, 15, 16, 255, 256, 2048, 4094, 4095], rng.integers(0, 4096, 15)])
-    tokens = np.unique(np.concatenate([chunk, np.arange(4096, inp.total_q)]))
-    check_call(dev, "mixed", "mixed_batch", tokens=tokens)
+    check_call(dev, "mixed", "mixed_batch")
 
 
 def test_mixed_graph_replay_reroutes_sequences():

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import paged_attention
+from oracle.parallel import paged_attention_parallel
 from paged_asymmetric_head_amd.synth import make_paged_inputs, workload
 from paged_asymmetric_head_amd.device import DeviceInputs
 from parity import compare, expected_counts, to_np
@@ -22,9 +22,10 @@ def say(msg):
 
 
 def oracle(inp, **kw):
+    """The FP64 oracle over the requested rows (default all), on every host core."""
     args = inp.oracle_kwargs()
     args.update(kw)
-    return paged_attention(**args)
+    return paged_attention_parallel(**args)
 
 
 def check_call(dev, entry, tag, tokens=None, **kw):
@@ -58,13 +59,12 @@ def test_workload_parity(name, entry):
     check_call(dev, entry, name)
 
 
-def test_chunked_prefill_parity_sampled_rows():
+def test_chunked_prefill_parity():
+    """The 4096-token chunk at 26624 cached tokens (Hq 32 / Hkv 2, FP8 K/V):
+    every output row against the oracle, the tolerance over the whole out."""
     inp = workload("chunked_prefill")
     dev = DeviceInputs(inp)
-    rng = np.random.default_rng(55)
-    tokens = np.unique(np.concatenate([[0, 1, 15, 16, 63, 64, 2047, 2048, 4031, 4094, 4095],
-                                       rng.integers(0, 4096, 21)]))
-    check_call(dev, "prefill", "chunked_prefill", tokens=tokens)
+    check_call(dev, "prefill", "chunked_prefill")
 
 
 # --- tiny grid through every entry that accepts it --------------------------------

@@ -316,6 +316,25 @@ def test_nan_partial_propagates_through_combine():
     assert np.isfinite(out[[0, 1, 1], [1, 0, 1]]).all()
 
 
+@pytest.mark.parametrize("tokens_per_item", [1, 3, 64])
+def test_parallel_runner_gives_the_rows_of_one_call(tokens_per_item):
+    """oracle.parallel cuts the rows into groups on threads; every row must be
+    the one a single paged_attention call gives (up to the rounding of the
+    key-range length each group's products run over), counts exactly."""
+    from oracle.parallel import paged_attention_parallel
+    inp = make_paged_inputs(33, seq_lens=[300, 41, 150], q_lens=[20, 1, 7], num_q_heads=8,
+                            num_kv_heads=2, page_size=16, kv_dtype="fp8", window=50, sinks=True,
+                            write_align=16)
+    ref = run(inp)
+    par = paged_attention_parallel(**inp.oracle_kwargs(), tokens_per_item=tokens_per_item, workers=4)
+    assert np.array_equal(par.tokens, ref.tokens) and np.array_equal(par.count, ref.count)
+    np.testing.assert_allclose(par.out, ref.out, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(par.lse, ref.lse, rtol=0, atol=1e-13)
+    sub = paged_attention_parallel(**inp.oracle_kwargs(), tokens=[27, 3, 0, 21], tokens_per_item=2)
+    assert list(sub.tokens) == [0, 3, 21, 27]
+    np.testing.assert_allclose(sub.out, ref.out[[0, 3, 21, 27]], rtol=0, atol=1e-13)
+
+
 def test_oracle_rejects_unreadable_visible_page():
     inp = make_paged_inputs(3, seq_lens=[20], q_lens=1, num_q_heads=1, num_kv_heads=1,
                             page_size=4, kv_dtype="bf16")
