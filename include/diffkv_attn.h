@@ -81,9 +81,9 @@ typedef struct diffkv_attn_desc {
   int32_t max_q_len;           /* >= every q_lens[b]; 1 for decode, <= 16 for verify */
   int32_t total_q;             /* == sum of q_lens: rows of q and out               */
   int32_t kv_dtype;            /* DIFFKV_KV_BF16 or DIFFKV_KV_FP8_E4M3              */
-  int32_t force_num_splits;    /* 0 = automatic; > 0 forces the key-axis split count
-                                  (decode, verify and mixed's split-KV part; a test
-                                  hook)                                             */
+  int32_t force_num_splits;    /* 0 = automatic; 1..65536 forces the key-axis split
+                                  count (decode, verify and mixed's split-KV part; a
+                                  test hook)                                        */
 } diffkv_attn_desc;
 
 /*

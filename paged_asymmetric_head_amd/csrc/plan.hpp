@@ -21,6 +21,7 @@ constexpr int kDefaultCUs = 256;     // MI355X: 256 compute units in 8 XCDs (the
                                      // when no device can be queried)
 constexpr int kMaxCUs = 1024;        // largest CU count a descriptor is validated for
 constexpr int kMaxGridYZ = 65535;
+constexpr int kMaxForcedSplits = 1 << 16;   // force_num_splits bound (a test hook)
 
 // Query rows per split-kernel workgroup: 16 * row_tiles, row_tiles in {1,2,4}.
 inline int split_row_tiles(int rows_per_pair) {

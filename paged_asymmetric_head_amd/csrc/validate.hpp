@@ -38,17 +38,21 @@ inline int validate_desc(const diffkv_attn_desc* d, int entry) {
   if ((long long)d->block_table_stride * d->page_size < d->max_seq_len) return DIFFKV_INVALID_ARGUMENT;
   if (d->total_q < d->batch || (long long)d->total_q > (long long)d->batch * d->max_q_len)
     return DIFFKV_INVALID_ARGUMENT;
-  if (d->force_num_splits < 0) return DIFFKV_INVALID_ARGUMENT;
+  if (d->force_num_splits < 0 || d->force_num_splits > kMaxForcedSplits) return DIFFKV_INVALID_ARGUMENT;
   if (entry == DIFFKV_ENTRY_DECODE && d->max_q_len != 1) return DIFFKV_INVALID_ARGUMENT;
   if (entry == DIFFKV_ENTRY_VERIFY && d->max_q_len > 16) return DIFFKV_INVALID_ARGUMENT;
-  // Launch-shape limits: grid y and z, the split grid's x, 32-bit element
-  // offsets into q and out, and the page offsets of the caches.
+  // Launch-shape limits: grid y and z, 32-bit element offsets into q and out
+  // (which also bound one sequence's query rows), then the split grid's x.
+  // The planner runs only on descriptors inside the first ones, so its
+  // 64-bit products cannot overflow.
   if ((long long)d->batch * d->num_kv_heads > kMaxGridYZ) return DIFFKV_UNSUPPORTED;
+  if ((long long)d->total_q * d->num_q_heads > (1LL << 31) / kHeadDimQK) return DIFFKV_UNSUPPORTED;
+  if ((long long)d->max_q_len * (d->num_q_heads / d->num_kv_heads) > (1LL << 31) / kHeadDimQK)
+    return DIFFKV_UNSUPPORTED;
   if (entry != DIFFKV_ENTRY_PREFILL) {
     const SplitPlan p = plan_split(split_part_desc(*d, entry), 0, kMaxCUs);
     if (p.grid_x > INT32_MAX) return DIFFKV_UNSUPPORTED;
   }
-  if ((long long)d->total_q * d->num_q_heads > (1LL << 31) / kHeadDimQK) return DIFFKV_UNSUPPORTED;
   return DIFFKV_OK;
 }
 
