@@ -18,16 +18,18 @@ at least 80 ms of their own calls (a long kernel's first launches after a
 pause run slower).
 
 One JSON line is printed.  `value` and `ms_per_step` come from the timed
-steps alone (HIP events around the K calls, no per-call instrumentation).
-`roofline` is the main attention kernel alone: a second pass of the same K
-calls has the library's dispatch stamp each main kernel with HIP events
-(diffkv_attn_profile_next_call); their mean is the kernel's duration (the
-median is reported beside it).
+steps (HIP events around the K calls).  `roofline` is the main attention
+kernel alone: in the same pass the library's dispatch stamps each call's main
+kernel with its own HIP events (diffkv_attn_profile_next_call); their mean is
+the kernel's duration (the median is reported beside it), and it never exceeds
+the step time.
 `roofline.stream_read` (decode and verify) is the achievable-bandwidth
 reference at the kernel's own byte count: a plain streaming read of that many
 bytes in one launch, cold, timed the same way; `kernel_frac_of_stream` is the
 attention kernel's rate as a fraction of it.
-`cpu_baseline` times the FP64 oracle on the host on a bounded sample.
+`cpu_baseline` times the FP64 oracle on the host's cores (every core of the
+process's affinity set, one thread each, BLAS held to one thread) on a bounded
+sample of the workload; every attention workload in `extra` carries its own.
 `extra` carries the other workloads measured the same way (mixed_batch: one
 serving step mixing a prefill chunk, verify blocks and decodes;
 batched_decode_sym: the decode batch with symmetric 128/128 heads), the paged KV
@@ -79,7 +81,9 @@ def parse_args():
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="target host time for the oracle sample")
+                    help="target host time for the headline's oracle sample")
+    ap.add_argument("--cpu-seconds-extra", type=float, default=4.0,
+                    help="target host time for each other workload's oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reads and writes 256 MiB), the "
                          "reference the HBM byte counters are scaled by")
@@ -199,9 +203,11 @@ EXTRA_WARM_MS = 80.0
 def time_calls(calls, steps, warmup, events, stream, warm_ms=0.0):
     """Warm up (`warmup` calls, then more until `warm_ms` milliseconds have
     passed), then time exactly `steps` calls (rotating over `calls`) with a
-    pair of HIP events around them; a second pass of the same calls has the
-    library stamp each main kernel's dispatch with its own pair of events.
-    Returns (total ms, wall seconds, sorted per-kernel ms)."""
+    pair of HIP events around them.  In the same pass the library stamps each
+    call's main kernel with its own pair of events at dispatch
+    (diffkv_attn_profile_next_call), so every kernel time lies inside the step
+    time it is reported beside.  Returns (total ms, wall seconds, sorted
+    per-kernel ms)."""
     import torch
     from paged_asymmetric_head_amd import binding as B
     n = len(calls)
@@ -220,15 +226,12 @@ def time_calls(calls, steps, warmup, events, stream, warm_ms=0.0):
     wall0 = time.perf_counter()
     events.record(t0, stream)
     for k in range(steps):
+        B.diffkv_attn_profile_next_call(pairs[k][0], pairs[k][1])
         calls[k % n]()
     events.record(t1, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = events.elapsed_ms(t0, t1)
-    for k in range(steps):
-        B.diffkv_attn_profile_next_call(pairs[k][0], pairs[k][1])
-        calls[k % n]()
-    torch.cuda.synchronize()
     kern = sorted(events.elapsed_ms(a, b) for a, b in pairs)
     return total_ms, wall, kern
 
@@ -652,54 +655,71 @@ def summary(m, sha, name):
     return res
 
 
-def cpu_baseline(name, seconds):
-    """The FP64 oracle on the host: whole query tokens of the workload until
-    about `seconds` of work, rate scaled to the metric's unit."""
+def _oracle_items(inp, entry):
+    """The workload cut into oracle items: every sequence with at most 16 new
+    tokens is one item (its tokens share one key range), longer ones are cut
+    into 8-token groups.  Each item is (packed rows, KV bytes of the union of
+    their visible keys, flops of their visible (row, key) pairs)."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    esize = 1 if inp.kv_dtype == "fp8" else 2
+    row_bytes = inp.num_kv_heads * (inp.q.shape[2] + inp.v_cache.shape[3]) * esize
+    starts = np.concatenate([[0], np.cumsum(inp.q_lens)[:-1]])
+    items = []
+    for b in range(inp.batch):
+        L, n = int(inp.seq_lens[b]), int(inp.q_lens[b])
+        step = n if n <= 16 else 8
+        for c0 in range(0, n, step):
+            i = np.arange(c0, min(n, c0 + step))
+            p = L - n + i
+            lo = np.maximum(0, p - inp.window + 1) if inp.window > 0 else np.zeros_like(p)
+            kv = int(p.max() + 1 - lo.min()) * row_bytes
+            flops = 2 * (inp.q.shape[2] + inp.v_cache.shape[3]) * int((p - lo + 1).sum()) * inp.num_q_heads
+            items.append((starts[b] + i, kv, flops))
+    return items
+
+
+def cpu_baseline(name, seconds):
+    """The FP64 oracle on the host: the workload's items (see _oracle_items)
+    in a fixed random order, one per thread on every core of the affinity set
+    (BLAS held to one thread each), in rounds of one item per core until about
+    `seconds` have passed; the rate is the sampled items' algorithmic work
+    (KV bytes, or flops for the prefill and mixed workloads) over the time."""
+    from concurrent.futures import ThreadPoolExecutor
+    import numpy as np
+    from threadpoolctl import threadpool_limits
     from oracle import paged_attention
+    from oracle.parallel import host_cores
     from paged_asymmetric_head_amd.synth import workload
 
     inp = workload(name)
     entry = ENTRY_OF[name]
     args = inp.oracle_kwargs()
-    starts = np.concatenate([[0], np.cumsum(inp.q_lens)[:-1]])
-    order = np.random.default_rng(0).permutation(inp.batch)
-    done_bytes = done_flops = 0
-    n_tok = passes = 0
-    t0 = time.perf_counter()
-    esize = 1 if inp.kv_dtype == "fp8" else 2
-    # Whole passes over the workload (in a fixed random sequence order) until
-    # the time budget is spent; a pass that does not fit stops mid-way.
-    while time.perf_counter() - t0 < seconds:
-        for b in order:
-            L, n = int(inp.seq_lens[b]), int(inp.q_lens[b])
-            chunk = n if entry != "prefill" else 8
-            for c0 in range(0, n, chunk):
-                toks = np.arange(starts[b] + c0, starts[b] + min(n, c0 + chunk))
-                paged_attention(**args, tokens=toks)
-                p = L - n + (toks - starts[b])
-                lo = np.maximum(0, p - inp.window + 1) if inp.window > 0 else np.zeros_like(p)
-                done_bytes += (int(p.max() + 1 - lo.min()) * inp.num_kv_heads
-                               * (inp.q.shape[2] + inp.v_cache.shape[3]) * esize)
-                done_flops += (2 * (inp.q.shape[2] + inp.v_cache.shape[3]) * int((p - lo + 1).sum())
-                               * inp.num_q_heads)
+    items = _oracle_items(inp, entry)
+    order = np.random.default_rng(0).permutation(len(items))
+    cores = host_cores()
+    done_kv = done_flops = n_items = n_tok = 0
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=cores) as ex:
+        t0 = time.perf_counter()
+        k = 0
+        while time.perf_counter() - t0 < seconds:
+            rnd = [items[order[(k + j) % len(items)]] for j in range(cores)]
+            list(ex.map(lambda it: paged_attention(**args, tokens=it[0]), rnd))
+            for toks, kv, fl in rnd:
+                done_kv += kv
+                done_flops += fl
                 n_tok += len(toks)
-                if time.perf_counter() - t0 >= seconds:
-                    break
-            if time.perf_counter() - t0 >= seconds:
-                break
-        else:
-            passes += 1
-    dt = time.perf_counter() - t0
-    threads = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
-    if entry == "prefill":
+            n_items += len(rnd)
+            k += cores
+        dt = time.perf_counter() - t0
+    if entry in ("prefill", "mixed"):
         val, unit = done_flops / dt / 1e12, "TFLOP/s"
     else:
-        val, unit = done_bytes / dt / 1e9, "GB/s"
-    return {"value": round(val, 6), "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": f"{name}: {n_tok} query tokens ({passes} whole passes over its {inp.total_q}), "
-                      f"all heads, in {dt:.1f} s (FP64 NumPy oracle, BLAS threads={threads})"}
+        val, unit = done_kv / dt / 1e9, "GB/s"
+    return {"value": round(val, 6), "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"{name}: {n_items} items ({n_tok} query tokens; an item is a sequence of up to "
+                      f"16 new tokens or 8 tokens of a longer one; the workload has {len(items)}), all "
+                      f"heads, in {dt:.1f} s: FP64 NumPy oracle, one thread per core on {cores} cores, "
+                      f"BLAS threads 1 each"}
 
 
 def main():
@@ -768,6 +788,9 @@ def main():
             print(f"[bench] {other}: generating and measuring", file=sys.stderr, flush=True)
             mo = measure(other, args.extra_steps, 5, events, warm_ms=EXTRA_WARM_MS)
             extra[other] = summary(mo, sha, other)
+            if not args.no_cpu_baseline:
+                print(f"[bench] {other}: timing the CPU oracle", file=sys.stderr, flush=True)
+                extra[other]["cpu_baseline"] = cpu_baseline(other, args.cpu_seconds_extra)
             if other == "verify_long":
                 with_stream_reference(extra[other]["roofline"], args.extra_steps, events)
             del mo
