@@ -179,6 +179,28 @@ int diffkv_attn_mixed(const diffkv_attn_desc* desc, const void* q, const void* k
                       hipStream_t stream);
 
 /*
+ * diffkv_attn_verify without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, layouts, results and errors
+ * are those of diffkv_attn_verify (bitwise the same output); the split-KV
+ * partials go to a static 32 MiB array the library holds on each device it
+ * runs on (zero-filled when the library loads, kept until the process ends).
+ * The call allocates and frees nothing.  A call whose split needs more than
+ * 32 MiB of workspace (264 bytes per partial row, so about 127K rows; the
+ * long-verify shape, 4 blocks of 8 tokens at GQA 8, needs 4.4 MB) returns
+ * DIFFKV_WORKSPACE_TOO_SMALL without launching.
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents: calls that overlap on one device (two streams, or two
+ * host threads) race and must be serialised by the caller.
+ */
+int diffkv_attn_verify_noalloc(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* q_lens, int32_t window,
+                               const float* sinks, float k_scale, float v_scale,
+                               float softmax_scale, void* out, float* lse_out, int32_t* count_out,
+                               hipStream_t stream);
+
+/*
  * Context partials (the key-range share of a context split across GPUs, each
  * holding a range of a sequence's keys; "diffbot/MiMo-V2.6-Flash-RL-FP8KV-
  * W4A8-2x-RTX-PRO-6000", What the kernels do: split-KV, here cut across key

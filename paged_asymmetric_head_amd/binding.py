@@ -54,6 +54,8 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = _ENTRY_ARGS
         fn.restype = ctypes.c_int
+    lib.diffkv_attn_verify_noalloc.argtypes = _ENTRY_ARGS[:15] + [ctypes.c_void_p]
+    lib.diffkv_attn_verify_noalloc.restype = ctypes.c_int
     lib.diffkv_kv_write.argtypes = [ctypes.POINTER(AttnDesc)] + [ctypes.c_void_p] * 7 + [
         ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
     lib.diffkv_attn_partial.argtypes = [ctypes.POINTER(AttnDesc)] + [ctypes.c_void_p] * 8 + [
@@ -166,6 +168,19 @@ def diffkv_attn_prefill(*args, **kwargs):
 
 def diffkv_attn_mixed(*args, **kwargs):
     _call("diffkv_attn_mixed", *args, **kwargs)
+
+
+def diffkv_attn_verify_noalloc(desc, q, k_cache, v_cache, block_table, seq_lens, q_lens, window,
+                               sinks, k_scale, v_scale, softmax_scale, out, lse_out=None,
+                               count_out=None, stream=None):
+    """diffkv_attn_verify on the library's static per-device workspace."""
+    status = load_library().diffkv_attn_verify_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(q_lens), int(window), _ptr(sinks), float(k_scale), float(v_scale),
+        float(softmax_scale), _ptr(out), _ptr(lse_out), _ptr(count_out), _stream(stream))
+    if status != OK:
+        raise DiffKVError(f"diffkv_attn_verify_noalloc: {diffkv_attn_strerror(status)} "
+                          f"(status {status})")
 
 
 def prepared_kv_write(desc, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_lens,

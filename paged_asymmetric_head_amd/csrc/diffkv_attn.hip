@@ -57,6 +57,53 @@ int stream_cu_count(hipStream_t stream) {
   return device_cu_count(dev);
 }
 
+// Workspace of diffkv_attn_verify_noalloc: one static array per device (the
+// code object's zero-filled data, held until the process ends), for callers
+// that cannot allocate.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address is looked up once per device, with
+// that device current, and only that address is ever passed to a kernel.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on device `dev` (nullptr if it cannot be
+// looked up).
+void* device_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) {
+      (void)hipGetLastError();
+      return;
+    }
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return;
+    }
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess)
+      g_scratch_ptr[dev] = ptr;
+    else
+      (void)hipGetLastError();
+    if (cur != dev) (void)hipSetDevice(cur);
+  });
+  return g_scratch_ptr[dev];
+}
+
+// Ordinal of the device a stream belongs to (the current device for the
+// null stream); -1 if it cannot be found.
+int stream_device(hipStream_t stream) {
+  int dev = -1;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) == hipSuccess) return dev;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  return dev;
+}
+
 // Disarms the profiling events when an entry point returns, so a call that
 // fails before its launch still consumes them (launch_main disarms them when
 // it dispatches with them).
@@ -405,6 +452,31 @@ int diffkv_attn_combine(int32_t num_parts, int32_t rows, int32_t num_q_heads,
   const hipError_t e = launch_main(reinterpret_cast<const void*>(&combine_kernel),
                                    dim3((unsigned)((rows + 3) / 4)), dim3(256), args, stream);
   return e == hipSuccess ? DIFFKV_OK : DIFFKV_HIP_ERROR;
+}
+
+int diffkv_attn_verify_noalloc(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* q_lens, int32_t window,
+                               const float* sinks, float k_scale, float v_scale,
+                               float softmax_scale, void* out, float* lse_out, int32_t* count_out,
+                               hipStream_t stream) {
+  const ProfileDisarm disarm;
+  const int st = validate_desc(desc, DIFFKV_ENTRY_VERIFY);
+  if (st != DIFFKV_OK) return st;
+  // The workspace this launch needs (the plan of the call itself, on the
+  // stream's device) must fit the static array; nothing is allocated.
+  const int dev = stream_device(stream);
+  const SplitPlan plan = plan_split(*desc, window, dev >= 0 ? device_cu_count(dev) : kDefaultCUs,
+                                    kLaunchSlots);
+  if (plan.workspace_bytes > kScratchBytes) return DIFFKV_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (plan.workspace_bytes > 0) {
+    ws = device_scratch(dev);
+    if (ws == nullptr) return DIFFKV_HIP_ERROR;
+  }
+  return run_entry(DIFFKV_ENTRY_VERIFY, desc, q, k_cache, v_cache, block_table, seq_lens, q_lens,
+                   window, sinks, k_scale, v_scale, softmax_scale, out, lse_out, count_out, ws,
+                   ws ? kScratchBytes : 0, stream);
 }
 
 int diffkv_attn_mixed(const diffkv_attn_desc* desc, const void* q, const void* k_cache,
