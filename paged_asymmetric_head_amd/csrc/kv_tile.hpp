@@ -97,7 +97,7 @@ struct KvTile {
   __device__ __forceinline__ void fetch_pages(int t, Pages& p) const {
     const int tc = min(t, t_last);
     if constexpr (UPAGE) {
-      p.k[0] = bt[(tc * kTileKeys) >> lp];
+      p.k[0] = scalar_load(bt, (tc * kTileKeys) >> lp);
       p.v[0] = p.k[0];
     } else {
 #pragma unroll

@@ -260,10 +260,10 @@ void split_attn_kernel(const SplitArgs a) {
   if constexpr (DIRECT) {
     b = blockIdx.x / a.n_qtiles;
     qt = blockIdx.x % a.n_qtiles;
-    L = a.seq_lens[b];
-    n = a.q_lens ? a.q_lens[b] : 1;
-    klo = a.key_lo ? a.key_lo[b] : 0;
-    khi = a.key_hi ? a.key_hi[b] : INT32_MAX;
+    L = scalar_load(a.seq_lens, b);
+    n = a.q_lens ? scalar_load(a.q_lens, b) : 1;
+    klo = a.key_lo ? scalar_load(a.key_lo, b) : 0;
+    khi = a.key_hi ? scalar_load(a.key_hi, b) : INT32_MAX;
     r0 = -1;                                  // summed below, after the loads are out
   } else {
     SplitPlanner<ROWS> plan(a);
