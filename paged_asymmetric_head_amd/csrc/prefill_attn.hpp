@@ -16,7 +16,19 @@
 //                    LDS read of the row-major V tile.
 // Each K or V^T fragment read from LDS feeds the MFMAs of both row tiles:
 // on gfx950 LDS read bandwidth, not the matrix cores, bounds a wave that
-// reads the whole tile for only 16 rows.
+// reads the whole tile for only 16 rows.  Even so the eight waves read 320 KB
+// of fragments from LDS per tile, about as long at the LDS's 128 bytes per
+// clock as the matrix products take, so neither unit is ever idle for long
+// without the other: the kernel runs at about 60% of both.
+// The two waves of a SIMD do not progress alike: the older one wins issue
+// ties, runs ahead through its phases and used to wait at the end-of-tile
+// barrier for about a fifth of each tile while the younger one finished
+// alone.  FP8 tiles are therefore gathered and widened by the four older
+// waves only (waves 0-3 pair with 4-7 on the four SIMDs), which takes that
+// work off the younger waves' path: 6% off the chunked-prefill workload,
+// bit-identical outputs.  (Raising the younger waves' priority instead makes
+// both waves move through the same phases together and was 7-16% slower.)
+// bf16 tiles have twice the register stage and keep the even split.
 // Only tiles that cross a row's causal or window boundary (or hold padding
 // rows) are masked; the others skip the compares.  The exp argument folds
 // the scale into one FMA on the raw score (the scale is positive), the row
@@ -49,7 +61,10 @@ template <bool FP8, bool UPAGE, bool COUNT, int DQK>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_attn_kernel(const SplitArgs a) {
   constexpr int QC = DQK / 32;               // 32-dim contraction steps of QK^T
-  using IO = KvTile<FP8, UPAGE, DQK, kPfThreads>;
+  // Threads that gather and widen the tiles: the older half of the waves
+  // for FP8, all of them for bf16.
+  constexpr int LT = FP8 ? kPfThreads / 2 : kPfThreads;
+  using IO = KvTile<FP8, UPAGE, DQK, LT>;
   constexpr int NS = FP8 ? DIFFKV_PREFILL_STAGES_FP8 : DIFFKV_PREFILL_STAGES_BF16;
   constexpr int RT = kPfRowTiles;
   constexpr int LDS_TILE = kKLdsElems<DQK> + kVLdsElems;
@@ -59,7 +74,10 @@ void prefill_attn_kernel(const SplitArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * LDS_TILE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // Wave-uniform (a scalar), so `loader` branches are scalar branches.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool loader = LT == kPfThreads || wave < kPfWaves / 2;
   const int col = lane & 15, grp = lane >> 4;
   const int qb = a.n_qtiles - 1 - (int)blockIdx.x;
   const int bg = blockIdx.y;
@@ -88,12 +106,14 @@ void prefill_attn_kernel(const SplitArgs a) {
   // NS register stages of gathered tiles; page ids NS tiles ahead of them.
   typename IO::Pages pg[NS];
   typename IO::Stage st[NS];
+  if (loader) {
 #pragma unroll
-  for (int i = 0; i < NS; ++i) io.fetch_pages(t_begin + i, pg[i]);
+    for (int i = 0; i < NS; ++i) io.fetch_pages(t_begin + i, pg[i]);
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    io.fetch_data(t_begin + i, pg[i], st[i]);
-    io.fetch_pages(t_begin + NS + i, pg[i]);
+    for (int i = 0; i < NS; ++i) {
+      io.fetch_data(t_begin + i, pg[i], st[i]);
+      io.fetch_pages(t_begin + NS + i, pg[i]);
+    }
   }
 
   const int r0 = seq_row_start(a.q_lens, b);
@@ -120,12 +140,12 @@ void prefill_attn_kernel(const SplitArgs a) {
 
   // Tile t lives in LDS buffer t & 1 and, before that, in register stage
   // (t - t_begin) % NS.  Tile t_begin goes to LDS now.
-  {
+  if (loader) {
     uint16_t* first = lds + (t_begin & 1) * LDS_TILE;
     io.store(st[0], first, first + kKLdsElems<DQK>);
+    io.fetch_data(t_begin + NS, pg[0], st[0]);
+    io.fetch_pages(t_begin + 2 * NS, pg[0]);
   }
-  io.fetch_data(t_begin + NS, pg[0], st[0]);
-  io.fetch_pages(t_begin + 2 * NS, pg[0]);
   __syncthreads();
 
   float m[RT], l[RT];
@@ -253,11 +273,13 @@ void prefill_attn_kernel(const SplitArgs a) {
       // Widen tile t + 1 into the other buffer (its last readers passed the
       // barrier that ended the previous tile), then start loading t + 1 + NS.
       const int j = (i + 1) % NS;   // a constant once the loop is unrolled
-      __builtin_amdgcn_s_setprio(1);
-      io.store(st[j], nxt, nxt + kKLdsElems<DQK>);
-      __builtin_amdgcn_s_setprio(0);
-      io.fetch_data(t + 1 + NS, pg[j], st[j]);
-      io.fetch_pages(t + 1 + 2 * NS, pg[j]);
+      if (loader) {
+        __builtin_amdgcn_s_setprio(1);
+        io.store(st[j], nxt, nxt + kKLdsElems<DQK>);
+        __builtin_amdgcn_s_setprio(0);
+        io.fetch_data(t + 1 + NS, pg[j], st[j]);
+        io.fetch_pages(t + 1 + 2 * NS, pg[j]);
+      }
       __syncthreads();
     }
   }
