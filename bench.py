@@ -21,7 +21,7 @@ One JSON line is printed.  `value` and `ms_per_step` come from the timed
 steps alone (HIP events around the K calls, nothing else on the stream).
 `roofline` is the main attention kernel alone: a second pass of the same K
 calls has the library's dispatch stamp each call's main kernel with its own
-HIP events (diffkv_attn_profile_next_call).  Their mean, bounded by the step
+HIP events (the descriptor's profile_start / profile_stop).  Their mean, bounded by the step
 time, is the kernel's duration `kernel_ms` (`kernel_ms_events` is the raw
 mean, `kernel_ms_median` the median).  The stamping itself adds time between
 launches, so the stamped pass's steps are not used for `value`.
@@ -207,7 +207,9 @@ def time_calls(calls, steps, warmup, events, stream, warm_ms=0.0):
     passed), then time exactly `steps` calls (rotating over `calls`) with a
     pair of HIP events around them and nothing else on the stream.  A second
     pass of the same calls has the library stamp each call's main kernel with
-    its own pair of events at dispatch (diffkv_attn_profile_next_call); that
+    its own pair of events at dispatch (the call's descriptor carries them
+    for that one call; a call without a descriptor, the combine, is one
+    kernel and is bracketed by the events on the stream instead); that
     stamping adds time between launches (the stamped pass's steps run longer),
     so the step time comes from the clean pass only.  Returns (total ms, wall
     seconds, sorted per-kernel ms, the stamped pass's total ms)."""
@@ -236,8 +238,18 @@ def time_calls(calls, steps, warmup, events, stream, warm_ms=0.0):
     total_ms = events.elapsed_ms(t0, t1)
     events.record(t2, stream)
     for k in range(steps):
-        B.diffkv_attn_profile_next_call(pairs[k][0], pairs[k][1])
-        calls[k % n]()
+        call = calls[k % n]
+        desc = getattr(call, "desc", None)
+        if desc is None:
+            events.record(pairs[k][0], stream)
+            call()
+            events.record(pairs[k][1], stream)
+        else:
+            B.set_profile_events(desc, pairs[k][0], pairs[k][1])
+            try:
+                call()
+            finally:
+                B.set_profile_events(desc, None, None)
     events.record(t3, stream)
     torch.cuda.synchronize()
     kern = sorted(events.elapsed_ms(a, b) for a, b in pairs)

@@ -84,6 +84,14 @@ typedef struct diffkv_attn_desc {
   int32_t force_num_splits;    /* 0 = automatic; 1..65536 forces the key-axis split
                                   count (decode, verify and mixed's split-KV part; a
                                   test hook)                                        */
+  /* Measurement hook: two caller-created HIP events, or both NULL.  When
+   * set, the call dispatches its first main kernel (not the split merge;
+   * for mixed, the split-KV kernel) with them as start and stop events
+   * (hipExtLaunchKernel), so hipEventElapsedTime(start, stop) is that
+   * kernel's execution time.  A call that fails before its launch leaves
+   * them as they were.  Exactly one NULL is DIFFKV_INVALID_ARGUMENT.       */
+  hipEvent_t profile_start;
+  hipEvent_t profile_stop;
 } diffkv_attn_desc;
 
 /*
@@ -120,8 +128,8 @@ typedef struct diffkv_attn_desc {
  *
  * Thread safety: every call is re-entrant.  The library's only state is the
  * compute-unit count of each device (filled once per device under
- * std::call_once) and the one-call profiling slot of each host thread
- * (diffkv_attn_profile_next_call, thread_local, empty unless armed).
+ * std::call_once), and the device address of the allocation-free verify
+ * entry's static workspace (also once per device).
  *
  * Preconditions on device data (undefined behaviour if broken):
  *   1 <= q_lens[b] <= seq_lens[b] <= max_seq_len, q_lens[b] <= max_q_len,
@@ -298,17 +306,6 @@ int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry);
  * for mixed, the bound of its split-KV part; 0 for an invalid descriptor.
  * Host only; for the current device's compute-unit count. */
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window);
-
-/* Profiling hook.  Arms two caller-created HIP events for the next
- * decode/verify/prefill/mixed/partial/combine/kv_write call made on this host
- * thread: that call's first main kernel (not the split merge; for mixed, the
- * split-KV kernel) is dispatched with them as its
- * start and stop events (hipExtLaunchKernel), so hipEventElapsedTime(start,
- * stop) is that kernel's execution time.  The hook disarms after one call,
- * also when that call returns an error before launching (the events are
- * then left as they were); passing two NULLs disarms it.  Returns DIFFKV_INVALID_ARGUMENT if exactly
- * one event is NULL. */
-int diffkv_attn_profile_next_call(hipEvent_t start, hipEvent_t stop);
 
 /* Static text for a status code. */
 const char* diffkv_attn_strerror(int status);

@@ -27,7 +27,7 @@ class AttnDesc(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "num_q_heads", "num_kv_heads", "head_dim_qk", "head_dim_v", "page_size",
         "num_pages", "block_table_stride", "max_seq_len", "max_q_len", "total_q", "kv_dtype",
-        "force_num_splits")]
+        "force_num_splits")] + [("profile_start", ctypes.c_void_p), ("profile_stop", ctypes.c_void_p)]
 
 
 def library_path():
@@ -72,8 +72,6 @@ def load_library():
     lib.diffkv_attn_validate.restype = ctypes.c_int
     lib.diffkv_attn_num_splits.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int, ctypes.c_int32]
     lib.diffkv_attn_num_splits.restype = ctypes.c_int
-    lib.diffkv_attn_profile_next_call.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    lib.diffkv_attn_profile_next_call.restype = ctypes.c_int
     lib.diffkv_attn_strerror.argtypes = [ctypes.c_int]
     lib.diffkv_attn_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -114,11 +112,12 @@ def diffkv_attn_num_splits(desc, entry, window=0):
     return int(load_library().diffkv_attn_num_splits(ctypes.byref(desc), int(entry), int(window)))
 
 
-def diffkv_attn_profile_next_call(start, stop):
-    """Arm two raw hipEvent_t handles (ints) around the next call's main kernel."""
-    status = load_library().diffkv_attn_profile_next_call(start, stop)
-    if status != OK:
-        raise DiffKVError(f"diffkv_attn_profile_next_call: {diffkv_attn_strerror(status)}")
+def set_profile_events(desc, start, stop):
+    """Put two raw hipEvent_t handles (ints), or two Nones, in the descriptor's
+    measurement fields: every call made with it then stamps its first main
+    kernel with them."""
+    desc.profile_start = start
+    desc.profile_stop = stop
 
 
 def prepared_call(name, desc, q, k_cache, v_cache, block_table, seq_lens, q_lens, window, sinks,
@@ -139,6 +138,7 @@ def prepared_call(name, desc, q, k_cache, v_cache, block_table, seq_lens, q_lens
         if status != OK:
             raise DiffKVError(f"{name}: {diffkv_attn_strerror(status)} (status {status})")
     call.keep_alive = keep
+    call.desc = desc
     return call
 
 
@@ -197,6 +197,7 @@ def prepared_kv_write(desc, k_new, v_new, k_cache, v_cache, block_table, seq_len
         if status != OK:
             raise DiffKVError(f"diffkv_kv_write: {diffkv_attn_strerror(status)} (status {status})")
     call.keep_alive = keep
+    call.desc = desc
     return call
 
 
@@ -225,9 +226,11 @@ def prepared_partial(desc, q, k_cache, v_cache, block_table, seq_lens, q_lens, k
             _ptr(seq_lens), _ptr(q_lens), _ptr(key_lo), _ptr(key_hi), int(window), float(k_scale),
             float(v_scale), float(softmax_scale), _ptr(out_part), _ptr(lse_part), _ptr(count_out),
             _ptr(workspace), int(workspace_bytes), _stream(stream))
-    return _prepared("diffkv_attn_partial", args,
+    call = _prepared("diffkv_attn_partial", args,
                      (desc, q, k_cache, v_cache, block_table, seq_lens, q_lens, key_lo, key_hi,
                       out_part, lse_part, count_out, workspace))
+    call.desc = desc
+    return call
 
 
 def prepared_combine(num_parts, rows, num_q_heads, out_parts, lse_parts, sinks, out,

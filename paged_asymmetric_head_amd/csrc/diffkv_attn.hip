@@ -22,10 +22,6 @@ using namespace diffkv;
 
 namespace {
 
-// Events armed by diffkv_attn_profile_next_call for this thread's next call.
-thread_local hipEvent_t g_profile_start = nullptr;
-thread_local hipEvent_t g_profile_stop = nullptr;
-
 // Compute units per device, queried once per device (the planner's one
 // resident round of workgroups is sized from it).  kDefaultCUs when the
 // device cannot be queried (no GPU, or an ordinal past kMaxDevices).
@@ -104,65 +100,64 @@ int stream_device(hipStream_t stream) {
   return dev;
 }
 
-// Disarms the profiling events when an entry point returns, so a call that
-// fails before its launch still consumes them (launch_main disarms them when
-// it dispatches with them).
-struct ProfileDisarm {
-  ~ProfileDisarm() { g_profile_start = g_profile_stop = nullptr; }
+// The measurement events of a call (the descriptor's profile_start and
+// profile_stop), or none.
+struct Profile {
+  hipEvent_t start = nullptr, stop = nullptr;
 };
 
-// Launches the main attention kernel of a call.  When profiling events are
-// armed, the dispatch itself stamps them (hipExtLaunchKernel), so their
-// elapsed time is the kernel's execution alone.
-hipError_t launch_main(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream) {
-  hipEvent_t start = g_profile_start, stop = g_profile_stop;
-  g_profile_start = g_profile_stop = nullptr;
-  if (start != nullptr)
-    return hipExtLaunchKernel(fn, grid, block, args, 0, stream, start, stop, 0);
+// Launches the main kernel of a call.  With measurement events, the
+// dispatch itself stamps them (hipExtLaunchKernel), so their elapsed time is
+// the kernel's execution alone.
+hipError_t launch_main(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream,
+                       const Profile& pf) {
+  if (pf.start != nullptr)
+    return hipExtLaunchKernel(fn, grid, block, args, 0, stream, pf.start, pf.stop, 0);
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 template <bool FP8, int RT, bool DIRECT, bool COUNT, bool UPAGE, int DQK>
-hipError_t launch_split_kernel(const SplitArgs& a, dim3 grid, hipStream_t stream) {
+hipError_t launch_split_kernel(const SplitArgs& a, dim3 grid, hipStream_t stream, const Profile& pf) {
   void* args[] = {const_cast<SplitArgs*>(&a)};
   constexpr int NS = kSplitStages<FP8>;
   return launch_main(
       reinterpret_cast<const void*>(&split_attn_kernel<FP8, RT, DIRECT, COUNT, UPAGE, NS, DQK>),
-      grid, dim3(256), args, stream);
+      grid, dim3(256), args, stream, pf);
 }
 
 template <bool FP8, int RT, bool UPAGE, int DQK>
-hipError_t dispatch_split_rt(const SplitArgs& a, dim3 grid, bool direct, bool count, hipStream_t st) {
-  if (direct) return count ? launch_split_kernel<FP8, RT, true, true, UPAGE, DQK>(a, grid, st)
-                           : launch_split_kernel<FP8, RT, true, false, UPAGE, DQK>(a, grid, st);
-  return count ? launch_split_kernel<FP8, RT, false, true, UPAGE, DQK>(a, grid, st)
-               : launch_split_kernel<FP8, RT, false, false, UPAGE, DQK>(a, grid, st);
+hipError_t dispatch_split_rt(const SplitArgs& a, dim3 grid, bool direct, bool count, hipStream_t st,
+                             const Profile& pf) {
+  if (direct) return count ? launch_split_kernel<FP8, RT, true, true, UPAGE, DQK>(a, grid, st, pf)
+                           : launch_split_kernel<FP8, RT, true, false, UPAGE, DQK>(a, grid, st, pf);
+  return count ? launch_split_kernel<FP8, RT, false, true, UPAGE, DQK>(a, grid, st, pf)
+               : launch_split_kernel<FP8, RT, false, false, UPAGE, DQK>(a, grid, st, pf);
 }
 
 // UPAGE: pages of at least one 64-key tile, so a tile never straddles pages.
 template <bool FP8, int DQK>
 hipError_t dispatch_split_dqk(const SplitArgs& a, int rt, bool upage, dim3 grid, bool direct,
-                              bool count, hipStream_t st) {
+                              bool count, hipStream_t st, const Profile& pf) {
   if (upage) {
     switch (rt) {
-      case 1: return dispatch_split_rt<FP8, 1, true, DQK>(a, grid, direct, count, st);
-      case 2: return dispatch_split_rt<FP8, 2, true, DQK>(a, grid, direct, count, st);
-      default: return dispatch_split_rt<FP8, 4, true, DQK>(a, grid, direct, count, st);
+      case 1: return dispatch_split_rt<FP8, 1, true, DQK>(a, grid, direct, count, st, pf);
+      case 2: return dispatch_split_rt<FP8, 2, true, DQK>(a, grid, direct, count, st, pf);
+      default: return dispatch_split_rt<FP8, 4, true, DQK>(a, grid, direct, count, st, pf);
     }
   }
   switch (rt) {
-    case 1: return dispatch_split_rt<FP8, 1, false, DQK>(a, grid, direct, count, st);
-    case 2: return dispatch_split_rt<FP8, 2, false, DQK>(a, grid, direct, count, st);
-    default: return dispatch_split_rt<FP8, 4, false, DQK>(a, grid, direct, count, st);
+    case 1: return dispatch_split_rt<FP8, 1, false, DQK>(a, grid, direct, count, st, pf);
+    case 2: return dispatch_split_rt<FP8, 2, false, DQK>(a, grid, direct, count, st, pf);
+    default: return dispatch_split_rt<FP8, 4, false, DQK>(a, grid, direct, count, st, pf);
   }
 }
 
 template <bool FP8>
 hipError_t dispatch_split(const SplitArgs& a, int dqk, int rt, bool upage, dim3 grid, bool direct,
-                          bool count, hipStream_t st) {
+                          bool count, hipStream_t st, const Profile& pf) {
   return dqk == kHeadDimQKSym
-             ? dispatch_split_dqk<FP8, kHeadDimQKSym>(a, rt, upage, grid, direct, count, st)
-             : dispatch_split_dqk<FP8, kHeadDimQK>(a, rt, upage, grid, direct, count, st);
+             ? dispatch_split_dqk<FP8, kHeadDimQKSym>(a, rt, upage, grid, direct, count, st, pf)
+             : dispatch_split_dqk<FP8, kHeadDimQK>(a, rt, upage, grid, direct, count, st, pf);
 }
 
 // Merge shape by the chunks a pair is expected to have: one wave with 16
@@ -198,26 +193,26 @@ hipError_t launch_merge(const SplitArgs& a, int rows, int max_chunks, dim3 grid,
 }
 
 template <bool FP8, bool UPAGE, bool COUNT, int DQK>
-hipError_t launch_prefill_kernel(const SplitArgs& a, dim3 grid, hipStream_t stream) {
+hipError_t launch_prefill_kernel(const SplitArgs& a, dim3 grid, hipStream_t stream, const Profile& pf) {
   void* args[] = {const_cast<SplitArgs*>(&a)};
   return launch_main(reinterpret_cast<const void*>(&prefill_attn_kernel<FP8, UPAGE, COUNT, DQK>),
-                     grid, dim3(kPfThreads), args, stream);
+                     grid, dim3(kPfThreads), args, stream, pf);
 }
 
 template <bool FP8, int DQK>
 hipError_t dispatch_prefill_dqk(const SplitArgs& a, bool upage, bool count, dim3 grid,
-                                hipStream_t st) {
-  if (upage) return count ? launch_prefill_kernel<FP8, true, true, DQK>(a, grid, st)
-                          : launch_prefill_kernel<FP8, true, false, DQK>(a, grid, st);
-  return count ? launch_prefill_kernel<FP8, false, true, DQK>(a, grid, st)
-               : launch_prefill_kernel<FP8, false, false, DQK>(a, grid, st);
+                                hipStream_t st, const Profile& pf) {
+  if (upage) return count ? launch_prefill_kernel<FP8, true, true, DQK>(a, grid, st, pf)
+                          : launch_prefill_kernel<FP8, true, false, DQK>(a, grid, st, pf);
+  return count ? launch_prefill_kernel<FP8, false, true, DQK>(a, grid, st, pf)
+               : launch_prefill_kernel<FP8, false, false, DQK>(a, grid, st, pf);
 }
 
 template <bool FP8>
 hipError_t dispatch_prefill(const SplitArgs& a, int dqk, bool upage, bool count, dim3 grid,
-                            hipStream_t st) {
-  return dqk == kHeadDimQKSym ? dispatch_prefill_dqk<FP8, kHeadDimQKSym>(a, upage, count, grid, st)
-                              : dispatch_prefill_dqk<FP8, kHeadDimQK>(a, upage, count, grid, st);
+                            hipStream_t st, const Profile& pf) {
+  return dqk == kHeadDimQKSym ? dispatch_prefill_dqk<FP8, kHeadDimQKSym>(a, upage, count, grid, st, pf)
+                              : dispatch_prefill_dqk<FP8, kHeadDimQK>(a, upage, count, grid, st, pf);
 }
 
 hipError_t launch_fill(int32_t* p, size_t n, hipStream_t stream) {
@@ -243,9 +238,10 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
               float v_scale, float softmax_scale, void* out, float* lse_out, int32_t* count_out,
               void* workspace, size_t workspace_bytes, hipStream_t stream,
               const PartialMode& pm = PartialMode()) {
-  const ProfileDisarm disarm;
   const int st = validate_desc(d, entry);
   if (st != DIFFKV_OK) return st;
+  // The measurement events go to the call's first main kernel.
+  const Profile pf{d->profile_start, d->profile_stop};
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !(out || pm.part_out))
     return DIFFKV_INVALID_ARGUMENT;
   if (!q_lens && d->max_q_len != 1) return DIFFKV_INVALID_ARGUMENT;
@@ -312,9 +308,9 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
     const dim3 grid((unsigned)plan.grid_x, d->num_kv_heads);
     hipError_t e =
         fp8 ? dispatch_split<true>(sa, d->head_dim_qk, plan.row_tiles, upage, grid, plan.direct, count,
-                                   stream)
+                                   stream, pf)
             : dispatch_split<false>(sa, d->head_dim_qk, plan.row_tiles, upage, grid, plan.direct, count,
-                                    stream);
+                                    stream, pf);
     if (e == hipSuccess && !plan.direct)
       e = launch_merge(sa, plan.rows, expected_chunks_per_pair(plan, *d),
                        dim3(sd.max_q_len * G, d->batch * d->num_kv_heads), stream);
@@ -330,8 +326,10 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
     pa.n_qtiles = prefill_row_blocks(*d);
     if (entry == DIFFKV_ENTRY_MIXED) pa.q_lo = kMixedSplitMaxQ + 1;
     const dim3 grid(pa.n_qtiles, d->batch * d->num_kv_heads);
-    const hipError_t e = fp8 ? dispatch_prefill<true>(pa, d->head_dim_qk, upage, count, grid, stream)
-                             : dispatch_prefill<false>(pa, d->head_dim_qk, upage, count, grid, stream);
+    // A mixed call's events went to its split-KV kernel.
+    const Profile ppf = entry == DIFFKV_ENTRY_PREFILL ? pf : Profile{};
+    const hipError_t e = fp8 ? dispatch_prefill<true>(pa, d->head_dim_qk, upage, count, grid, stream, ppf)
+                             : dispatch_prefill<false>(pa, d->head_dim_qk, upage, count, grid, stream, ppf);
     if (e != hipSuccess) return DIFFKV_HIP_ERROR;
   }
   return DIFFKV_OK;
@@ -340,7 +338,6 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
 int run_kv_write(const diffkv_attn_desc* d, const void* k_new, const void* v_new, void* k_cache,
                  void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                  const int32_t* q_lens, float k_scale, float v_scale, hipStream_t stream) {
-  const ProfileDisarm disarm;
   const int st = validate_desc(d, DIFFKV_ENTRY_PREFILL);
   if (st != DIFFKV_OK) return st;
   if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !seq_lens)
@@ -372,8 +369,10 @@ int run_kv_write(const diffkv_attn_desc* d, const void* k_new, const void* v_new
                               : reinterpret_cast<const void*>(&kv_write_kernel<true, kHeadDimQK>))
                        : (sym ? reinterpret_cast<const void*>(&kv_write_kernel<false, kHeadDimQKSym>)
                               : reinterpret_cast<const void*>(&kv_write_kernel<false, kHeadDimQK>));
-  return launch_main(fn, grid, dim3(256), args, stream) == hipSuccess ? DIFFKV_OK
-                                                                       : DIFFKV_HIP_ERROR;
+  return launch_main(fn, grid, dim3(256), args, stream, Profile{d->profile_start, d->profile_stop}) ==
+                 hipSuccess
+             ? DIFFKV_OK
+             : DIFFKV_HIP_ERROR;
 }
 
 }  // namespace
@@ -427,7 +426,6 @@ int diffkv_attn_partial(const diffkv_attn_desc* desc, const void* q, const void*
                         int32_t window, float k_scale, float v_scale, float softmax_scale,
                         float* out_part, float* lse_part, int32_t* count_out, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
-  const ProfileDisarm disarm;
   if (out_part == nullptr || lse_part == nullptr) return DIFFKV_INVALID_ARGUMENT;
   PartialMode pm;
   pm.key_lo = key_lo;
@@ -441,7 +439,6 @@ int diffkv_attn_partial(const diffkv_attn_desc* desc, const void* q, const void*
 int diffkv_attn_combine(int32_t num_parts, int32_t rows, int32_t num_q_heads,
                         const float* out_parts, const float* lse_parts, const float* sinks,
                         void* out, float* lse_out, hipStream_t stream) {
-  const ProfileDisarm disarm;
   if (num_parts < 1 || rows < 1 || num_q_heads < 1 || rows % num_q_heads != 0)
     return DIFFKV_INVALID_ARGUMENT;
   if (num_parts > kMaxCombineParts) return DIFFKV_UNSUPPORTED;
@@ -449,8 +446,8 @@ int diffkv_attn_combine(int32_t num_parts, int32_t rows, int32_t num_q_heads,
   CombineArgs a{out_parts, lse_parts, sinks, static_cast<uint16_t*>(out), lse_out,
                 num_parts, rows, num_q_heads};
   void* args[] = {&a};
-  const hipError_t e = launch_main(reinterpret_cast<const void*>(&combine_kernel),
-                                   dim3((unsigned)((rows + 3) / 4)), dim3(256), args, stream);
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&combine_kernel),
+                                       dim3((unsigned)((rows + 3) / 4)), dim3(256), args, 0, stream);
   return e == hipSuccess ? DIFFKV_OK : DIFFKV_HIP_ERROR;
 }
 
@@ -460,7 +457,6 @@ int diffkv_attn_verify_noalloc(const diffkv_attn_desc* desc, const void* q, cons
                                const float* sinks, float k_scale, float v_scale,
                                float softmax_scale, void* out, float* lse_out, int32_t* count_out,
                                hipStream_t stream) {
-  const ProfileDisarm disarm;
   const int st = validate_desc(desc, DIFFKV_ENTRY_VERIFY);
   if (st != DIFFKV_OK) return st;
   // The workspace this launch needs (the plan of the call itself, on the
@@ -505,13 +501,6 @@ int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t wind
   if (entry == DIFFKV_ENTRY_PREFILL) return 1;
   return plan_split(split_part_desc(*desc, entry), window, stream_cu_count(nullptr), kLaunchSlots)
       .max_chunks;
-}
-
-int diffkv_attn_profile_next_call(hipEvent_t start, hipEvent_t stop) {
-  if ((start == nullptr) != (stop == nullptr)) return DIFFKV_INVALID_ARGUMENT;
-  g_profile_start = start;
-  g_profile_stop = stop;
-  return DIFFKV_OK;
 }
 
 const char* diffkv_attn_strerror(int status) {

@@ -39,6 +39,7 @@ inline int validate_desc(const diffkv_attn_desc* d, int entry) {
   if (d->total_q < d->batch || (long long)d->total_q > (long long)d->batch * d->max_q_len)
     return DIFFKV_INVALID_ARGUMENT;
   if (d->force_num_splits < 0 || d->force_num_splits > kMaxForcedSplits) return DIFFKV_INVALID_ARGUMENT;
+  if ((d->profile_start == nullptr) != (d->profile_stop == nullptr)) return DIFFKV_INVALID_ARGUMENT;
   if (entry == DIFFKV_ENTRY_DECODE && d->max_q_len != 1) return DIFFKV_INVALID_ARGUMENT;
   if (entry == DIFFKV_ENTRY_VERIFY && d->max_q_len > 16) return DIFFKV_INVALID_ARGUMENT;
   // Launch-shape limits: grid y and z, 32-bit element offsets into q and out

@@ -199,10 +199,13 @@ def test_stream_reference_library_loads_and_rejects_bad_arguments():
     assert fn(16, 16, 16, 1, 5, None) == 1              # unsupported loads per thread
 
 
-def test_profile_hook_rejects_one_null_event(lib):
-    """Arming takes both events or neither (host only: the handles are only
-    stored, never used, and the last call disarms)."""
+def test_measurement_events_come_in_pairs(lib):
+    """The descriptor's measurement events are both set or both NULL (host
+    only: the handles are checked, never used, by the validation)."""
+    d = good_desc()
+    assert B.diffkv_attn_validate(d, B.ENTRY_VERIFY) == B.OK
     fake = 256
-    assert lib.diffkv_attn_profile_next_call(fake, None) == B.INVALID_ARGUMENT
-    assert lib.diffkv_attn_profile_next_call(None, fake) == B.INVALID_ARGUMENT
-    assert lib.diffkv_attn_profile_next_call(None, None) == B.OK
+    for start, stop, want in ((fake, None, B.INVALID_ARGUMENT), (None, fake, B.INVALID_ARGUMENT),
+                              (fake, fake + 8, B.OK), (None, None, B.OK)):
+        B.set_profile_events(d, start, stop)
+        assert B.diffkv_attn_validate(d, B.ENTRY_VERIFY) == want, (start, stop)

@@ -1,8 +1,8 @@
-"""The profiling hook (diffkv_attn_profile_next_call): armed events are
-stamped by the next call's main kernel (a positive duration no longer than
-the host's wall time around the call), and a call that fails its argument
-checks consumes the hook without touching the events, so the call after it
-leaves them as they were."""
+"""The measurement events of the call descriptor (profile_start /
+profile_stop): a call made with them stamps its main kernel (a positive
+duration no longer than the host's wall time around the call); a call that
+fails its argument checks leaves them untouched, and a call made with the
+fields cleared again records nothing in them."""
 
 import ctypes
 import time
@@ -43,7 +43,7 @@ class Events:
             self.hip.hipEventDestroy(ctypes.c_void_p(ev))
 
 
-def test_armed_events_time_the_main_kernel_and_a_failed_call_disarms():
+def test_descriptor_events_time_the_main_kernel():
     lens = [9000, 7000, 8000, 6500]
     inp = make_paged_inputs(71, seq_lens=lens, q_lens=8, num_q_heads=8, num_kv_heads=1,
                             page_size=128, kv_dtype="bf16", sinks=True)
@@ -52,10 +52,10 @@ def test_armed_events_time_the_main_kernel_and_a_failed_call_disarms():
     stream = torch.cuda.current_stream().cuda_stream
     ev = Events()
     try:
-        print("[gpu] profile hook: armed verify call", flush=True)
+        print("[gpu] measurement events: verify call with events", flush=True)
         s1, e1 = ev.create(), ev.create()
         torch.cuda.synchronize()
-        B.diffkv_attn_profile_next_call(s1, e1)
+        B.set_profile_events(call.desc, s1, e1)
         t0 = time.perf_counter()
         call()
         torch.cuda.synchronize()
@@ -63,23 +63,25 @@ def test_armed_events_time_the_main_kernel_and_a_failed_call_disarms():
         ms = ev.elapsed_ms(s1, e1)
         assert 0.0 < ms <= wall_ms
 
-        print("[gpu] profile hook: failed call, then an unarmed verify call", flush=True)
+        print("[gpu] measurement events: failed call, then a call without events", flush=True)
         s2, e2 = ev.create(), ev.create()
         ev.record(s2, stream)
         ev.record(e2, stream)
         torch.cuda.synchronize()
         before = ev.elapsed_ms(s2, e2)
-        B.diffkv_attn_profile_next_call(s2, e2)
         bad = dev.desc("verify")
+        B.set_profile_events(bad, s2, e2)
         bad.max_q_len = 17                         # over the verify limit: rejected before any launch
         lib = B.load_library()
         st = lib.diffkv_attn_verify(ctypes.byref(bad), None, None, None, None, None, None, 0, None,
                                     1.0, 1.0, 1.0, None, None, None, None, 0, None)
         assert st == B.INVALID_ARGUMENT
-        call()                                     # would re-stamp s2 / e2 if the hook were still armed
+        B.set_profile_events(call.desc, None, None)
+        call()                                     # records nothing in s2 / e2 (or s1 / e1)
         torch.cuda.synchronize()
         assert ev.elapsed_ms(s2, e2) == before
+        assert ev.elapsed_ms(s1, e1) == ms
     finally:
-        B.diffkv_attn_profile_next_call(None, None)
+        B.set_profile_events(call.desc, None, None)
         torch.cuda.synchronize()
         ev.close()
