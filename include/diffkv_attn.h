@@ -131,7 +131,8 @@ typedef struct diffkv_attn_desc {
  * std::call_once), and the device address of the allocation-free verify
  * entry's static workspace (also once per device).
  *
- * Preconditions on device data (undefined behaviour if broken):
+ * Preconditions on device data (undefined behaviour if broken; the debug
+ * build checks them, see diffkv_attn_debug_flags):
  *   1 <= q_lens[b] <= seq_lens[b] <= max_seq_len, q_lens[b] <= max_q_len,
  *   sum(q_lens) == total_q, and every block-table entry that is read lies in
  *   [0, num_pages).  Slots the rows cannot see may hold anything, NaN
@@ -306,6 +307,19 @@ int diffkv_attn_validate(const diffkv_attn_desc* desc, int entry);
  * for mixed, the bound of its split-KV part; 0 for an invalid descriptor.
  * Host only; for the current device's compute-unit count. */
 int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t window);
+
+/* Debug builds only (the library compiled with -DDIFFKV_DEBUG, shipped as
+ * libdiffkv_attn_debug.so).  Their kernels check the preconditions on device
+ * data above (1 <= q_lens[b] <= seq_lens[b] <= max_seq_len, q_lens[b] <=
+ * max_q_len, sum(q_lens) == total_q, every block-table entry read in
+ * [0, num_pages)); a violation sets a bit in a device-wide word (1: a q_len,
+ * 2: a seq_len, 4: a block-table entry, 8: the row total) and the offending
+ * value is replaced by one that keeps every memory access in bounds, so the
+ * call completes with a meaningless result rather than fault.  This call
+ * enqueues on `stream` a copy of that word to the caller's device word
+ * `flags` and clears it.  Release builds return DIFFKV_UNSUPPORTED and
+ * enqueue nothing; NULL flags is DIFFKV_INVALID_ARGUMENT. */
+int diffkv_attn_debug_flags(uint32_t* flags, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* diffkv_attn_strerror(int status);

@@ -30,8 +30,23 @@ class AttnDesc(ctypes.Structure):
         "force_num_splits")] + [("profile_start", ctypes.c_void_p), ("profile_stop", ctypes.c_void_p)]
 
 
+_LIBRARY_FILES = {"release": "libdiffkv_attn.so", "debug": "libdiffkv_attn_debug.so"}
+_VARIANT = "release"
+
+
 def library_path():
-    return os.path.join(_HERE, "libdiffkv_attn.so")
+    return os.path.join(_HERE, _LIBRARY_FILES[_VARIANT])
+
+
+def select_library(variant):
+    """Which build later calls open: "release" (the default) or "debug" (the
+    same library with the device-side precondition checks compiled in; see
+    diffkv_attn_debug_flags).  Calls prepared earlier keep their library."""
+    global _VARIANT, _LIB
+    if variant not in _LIBRARY_FILES:
+        raise ValueError(f"unknown library variant {variant!r}")
+    if variant != _VARIANT:
+        _VARIANT, _LIB = variant, None
 
 
 _ENTRY_ARGS = [ctypes.POINTER(AttnDesc)] + [ctypes.c_void_p] * 6 + [
@@ -72,6 +87,8 @@ def load_library():
     lib.diffkv_attn_validate.restype = ctypes.c_int
     lib.diffkv_attn_num_splits.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int, ctypes.c_int32]
     lib.diffkv_attn_num_splits.restype = ctypes.c_int
+    lib.diffkv_attn_debug_flags.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.diffkv_attn_debug_flags.restype = ctypes.c_int
     lib.diffkv_attn_strerror.argtypes = [ctypes.c_int]
     lib.diffkv_attn_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -110,6 +127,13 @@ def diffkv_attn_workspace_bytes(desc, entry):
 
 def diffkv_attn_num_splits(desc, entry, window=0):
     return int(load_library().diffkv_attn_num_splits(ctypes.byref(desc), int(entry), int(window)))
+
+
+def diffkv_attn_debug_flags(flags, stream=None):
+    """Enqueue the copy of the debug build's violation bits into `flags` (a
+    one-element int32 device tensor) and clear them; returns the status
+    (UNSUPPORTED from a release build, which enqueues nothing)."""
+    return int(load_library().diffkv_attn_debug_flags(_ptr(flags), _stream(stream)))
 
 
 def set_profile_events(desc, start, stop):

@@ -1,6 +1,7 @@
-"""Builds libdiffkv_attn.so (the attention library) and libdiffkv_stream.so
-(the streaming-read reference the benchmark quotes beside HBM peak) in-tree
-with hipcc for gfx950.
+"""Builds libdiffkv_attn.so (the attention library), libdiffkv_attn_debug.so
+(the same library with the device-side precondition checks compiled in,
+-DDIFFKV_DEBUG) and libdiffkv_stream.so (the streaming-read reference the
+benchmark quotes beside HBM peak) in-tree with hipcc for gfx950.
 
     python -m paged_asymmetric_head_amd.build
 
@@ -17,6 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUTPUT = os.path.join(HERE, "libdiffkv_attn.so")
+DEBUG_OUTPUT = os.path.join(HERE, "libdiffkv_attn_debug.so")
 SOURCES = [os.path.join(CSRC, "diffkv_attn.hip")]
 STREAM_OUTPUT = os.path.join(HERE, "libdiffkv_stream.so")
 STREAM_SOURCES = [os.path.join(CSRC, "stream_read.hip")]
@@ -37,9 +39,9 @@ def command(output=OUTPUT, extra=(), sources=SOURCES):
             *extra, "-o", output, *sources]
 
 
-def _compile(output, sources, verbose):
+def _compile(output, sources, verbose, extra=()):
     tmp = output + ".tmp"
-    cmd = command(tmp, sources=sources)
+    cmd = command(tmp, extra=extra, sources=sources)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,8 +52,9 @@ def _compile(output, sources, verbose):
 
 
 def build(verbose=False):
-    """Compile both libraries; returns the attention library's path."""
+    """Compile the libraries; returns the attention library's path."""
     _compile(OUTPUT, SOURCES, verbose)
+    _compile(DEBUG_OUTPUT, SOURCES, verbose, extra=("-DDIFFKV_DEBUG",))
     _compile(STREAM_OUTPUT, STREAM_SOURCES, verbose)
     return OUTPUT
 

@@ -145,6 +145,21 @@ __device__ __forceinline__ int32_t scalar_load(const int32_t* p, long long i) {
   return ((const_i32*)p)[i];
 }
 
+// Debug builds (-DDIFFKV_DEBUG) check the preconditions on device data that
+// the host cannot see: each violation sets a bit in a device-wide word (read
+// and cleared by diffkv_attn_debug_flags) and the offending value is replaced
+// by one that keeps every access in bounds, so the call finishes with a
+// meaningless result instead of touching memory it must not.  Release
+// builds compile none of this.
+#ifdef DIFFKV_DEBUG
+__device__ uint32_t g_debug_flags;
+constexpr uint32_t kDbgQLen = 1;      // q_len outside [1, seq_len] or above max_q_len
+constexpr uint32_t kDbgSeqLen = 2;    // seq_len outside [0, max_seq_len]
+constexpr uint32_t kDbgPage = 4;      // a block-table entry read outside [0, num_pages)
+constexpr uint32_t kDbgRows = 8;      // sum(q_lens) != total_q (a row outside [0, total_q))
+__device__ __forceinline__ void debug_flag(uint32_t bits) { atomicOr(&g_debug_flags, bits); }
+#endif
+
 // Value of x in lane `lane` (wave-uniform) for every lane.
 __device__ __forceinline__ int read_lane(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
 

@@ -22,6 +22,15 @@ using namespace diffkv;
 
 namespace {
 
+#ifdef DIFFKV_DEBUG
+// Copies the debug builds' violation bits to the caller's word and clears
+// them (a kernel, so the call stays in stream order and capturable).
+__global__ void take_debug_flags_kernel(uint32_t* flags) {
+  *flags = g_debug_flags;
+  g_debug_flags = 0;
+}
+#endif
+
 // Compute units per device, queried once per device (the planner's one
 // resident round of workgroups is sized from it).  kDefaultCUs when the
 // device cannot be queried (no GPU, or an ordinal past kMaxDevices).
@@ -285,6 +294,12 @@ int run_entry(int entry, const diffkv_attn_desc* d, const void* q, const void* k
   a.part_out = pm.part_out;
   a.scale_log2 = softmax_scale * ks * kLog2e;
   a.v_scale = vs;
+#ifdef DIFFKV_DEBUG
+  a.max_seq_len = d->max_seq_len;
+  a.max_q_len = d->max_q_len;
+  a.total_q = d->total_q;
+  a.num_pages = d->num_pages;
+#endif
 
   // Split-KV part: decode and verify, and a mixed call's short sequences.
   if (entry != DIFFKV_ENTRY_PREFILL) {
@@ -501,6 +516,21 @@ int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t wind
   if (entry == DIFFKV_ENTRY_PREFILL) return 1;
   return plan_split(split_part_desc(*desc, entry), window, stream_cu_count(nullptr), kLaunchSlots)
       .max_chunks;
+}
+
+int diffkv_attn_debug_flags(uint32_t* flags, hipStream_t stream) {
+#ifdef DIFFKV_DEBUG
+  if (flags == nullptr) return DIFFKV_INVALID_ARGUMENT;
+  void* args[] = {&flags};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&take_debug_flags_kernel), dim3(1), dim3(1),
+                         args, 0, stream) == hipSuccess
+             ? DIFFKV_OK
+             : DIFFKV_HIP_ERROR;
+#else
+  (void)flags;
+  (void)stream;
+  return DIFFKV_UNSUPPORTED;
+#endif
 }
 
 const char* diffkv_attn_strerror(int status) {

@@ -58,13 +58,17 @@ struct KvTile {
   size_t k_slot_bytes, v_slot_bytes;   // Hkv rows per slot
   int lp, pmask, kv_lo, kv_hi, t_last, tid;
   int koff;                  // first key of this loader's slice in each tile
+#ifdef DIFFKV_DEBUG
+  int num_pages = 1;         // entries outside [0, num_pages) read page 0
+#endif
   // Large pages: byte offset of each of this thread's units from the tile's
   // first slot (the tile lies inside one page, so rows are slot-contiguous).
   uint32_t k_off[UPAGE ? KU : 1], v_off[UPAGE ? VU : 1];
 
   __device__ __forceinline__ KvTile(const uint8_t* k_cache, const uint8_t* v_cache,
                                     const int32_t* bt_row, int hkv, int g, int log2_page,
-                                    int lo, int hi, int t_end, int thread, int key_off = 0)
+                                    int lo, int hi, int t_end, int thread, int key_off = 0,
+                                    int pages = 1)
       : k_head(k_cache + (size_t)g * DQK * ESZ),
         v_head(v_cache + (size_t)g * kHeadDimV * ESZ),
         bt(bt_row),
@@ -72,6 +76,11 @@ struct KvTile {
         v_slot_bytes((size_t)hkv * kHeadDimV * ESZ),
         lp(log2_page), pmask((1 << log2_page) - 1), kv_lo(lo), kv_hi(hi), t_last(t_end - 1),
         tid(thread), koff(key_off) {
+#ifdef DIFFKV_DEBUG
+    num_pages = pages;
+#else
+    (void)pages;
+#endif
     if constexpr (UPAGE) {
 #pragma unroll
       for (int k = 0; k < KU; ++k) k_off[k] = (uint32_t)(k_row(k) * k_slot_bytes + k_piece(k) * 16);
@@ -111,6 +120,18 @@ struct KvTile {
         p.v[k] = bt[(readable(j) ? j : kv_lo) >> lp];
       }
     }
+#ifdef DIFFKV_DEBUG
+    auto check = [&](int& page) {
+      if ((unsigned)page >= (unsigned)num_pages) {
+        debug_flag(kDbgPage);
+        page = 0;
+      }
+    };
+#pragma unroll
+    for (int k = 0; k < NPK; ++k) check(p.k[k]);
+#pragma unroll
+    for (int k = 0; k < NPV; ++k) check(p.v[k]);
+#endif
   }
 
   // Gather tile t's K and V rows into registers.

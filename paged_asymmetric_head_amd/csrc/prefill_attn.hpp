@@ -84,8 +84,14 @@ void prefill_attn_kernel(const SplitArgs a) {
   const int b = bg / a.hkv, g = bg % a.hkv;
   const int G = a.group;
 
+#ifdef DIFFKV_DEBUG
+  int L = a.seq_lens[b];
+  int n = a.q_lens ? a.q_lens[b] : 1;
+  DIFFKV_CHECK_LENGTHS(a, L, n);
+#else
   const int L = a.seq_lens[b];
   const int n = a.q_lens ? a.q_lens[b] : 1;
+#endif
   if (qb * kPrefillRows >= n * G || n < a.q_lo || n > a.q_hi) return;
   int kv_lo, kv_hi;
   qtile_key_range(L, n, G, qb, kPrefillRows, a.window, kv_lo, kv_hi);
@@ -102,7 +108,7 @@ void prefill_attn_kernel(const SplitArgs a) {
   const int lo_last = a.window > 0 ? max(0, p_last - a.window + 1) : 0;
 
   const IO io(a.k_cache, a.v_cache, a.block_table + (size_t)b * a.bt_stride, a.hkv, g,
-              a.log2_page, kv_lo, kv_hi, t_end, tid);
+              a.log2_page, kv_lo, kv_hi, t_end, tid, 0, DIFFKV_PAGES(a));
   // NS register stages of gathered tiles; page ids NS tiles ahead of them.
   typename IO::Pages pg[NS];
   typename IO::Stage st[NS];
@@ -117,6 +123,9 @@ void prefill_attn_kernel(const SplitArgs a) {
   }
 
   const int r0 = seq_row_start(a.q_lens, b);
+#ifdef DIFFKV_DEBUG
+  if (qb == 0) DIFFKV_CHECK_TOTAL_ROWS(a, b, r0, n);
+#endif
 
   // This lane's query row in each of the wave's row tiles.
   bool row_ok[RT];
@@ -125,7 +134,7 @@ void prefill_attn_kernel(const SplitArgs a) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int R = r_first + (wave * RT + rt) * 16 + col;
-    row_ok[rt] = R < n * G;
+    row_ok[rt] = R < n * G && DIFFKV_ROW_IN_RANGE(a, r0 + R / G);
     tok[rt] = row_ok[rt] ? R / G : 0;
     hh[rt] = g * G + (row_ok[rt] ? R % G : 0);
     const int p_row = L - n + tok[rt];

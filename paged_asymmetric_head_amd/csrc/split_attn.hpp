@@ -63,7 +63,48 @@ struct SplitArgs {
   int q_lo, q_hi;     // this launch takes the sequences with q_lo <= q_len <= q_hi
   float scale_log2;   // softmax_scale * k_scale * log2(e)
   float v_scale;      // v_scale for FP8 caches, 1 for bf16
+#ifdef DIFFKV_DEBUG
+  int max_seq_len, max_q_len, total_q, num_pages;   // the descriptor's bounds
+#endif
 };
+
+// Debug builds (-DDIFFKV_DEBUG) check a sequence's lengths against the
+// descriptor's bounds and make them safe (seq_len clamped to [0,
+// max_seq_len], q_len to at most seq_len, so no position is negative and no
+// block-table index passes the row), drop packed rows outside [0, total_q),
+// let the last sequence's workgroup check that the rows add up to total_q,
+// and bound block-table entries by the page count.  In release builds the
+// macros below expand to nothing (or to true), so the kernels are the same
+// code as without them.
+#ifdef DIFFKV_DEBUG
+__device__ __forceinline__ void check_lengths(const SplitArgs& a, int& L, int& n) {
+  uint32_t bad = 0;
+  if (L < 0 || L > a.max_seq_len) {
+    bad |= kDbgSeqLen;
+    L = min(max(L, 0), a.max_seq_len);
+  }
+  if (n < 1 || n > L || n > a.max_q_len) bad |= kDbgQLen;
+  if (n > L) n = L;
+  if (bad) debug_flag(bad);
+}
+__device__ __forceinline__ bool row_in_range(const SplitArgs& a, int row) {
+  if ((unsigned)row < (unsigned)a.total_q) return true;
+  debug_flag(kDbgRows);
+  return false;
+}
+__device__ __forceinline__ void check_total_rows(const SplitArgs& a, int b, int r0, int n) {
+  if (b == a.batch - 1 && threadIdx.x == 0 && r0 + n != a.total_q) debug_flag(kDbgRows);
+}
+#define DIFFKV_CHECK_LENGTHS(a, L, n) check_lengths(a, L, n)
+#define DIFFKV_ROW_IN_RANGE(a, row) row_in_range(a, row)
+#define DIFFKV_CHECK_TOTAL_ROWS(a, b, r0, n) check_total_rows(a, b, r0, n)
+#define DIFFKV_PAGES(a) (a).num_pages
+#else
+#define DIFFKV_CHECK_LENGTHS(a, L, n) ((void)0)
+#define DIFFKV_ROW_IN_RANGE(a, row) true
+#define DIFFKV_CHECK_TOTAL_ROWS(a, b, r0, n) ((void)0)
+#define DIFFKV_PAGES(a) 1
+#endif
 
 // Tiles of chunk s among S equal shares of the aligned tile range.
 __device__ __forceinline__ void split_tiles(int kv_lo, int kv_hi, int S, int s, int& t_begin,
@@ -110,6 +151,7 @@ struct SplitPlanner {
       n = a.q_lens ? a.q_lens[b] : 1;
       if (a.key_lo) klo = a.key_lo[b];
       if (a.key_hi) khi = a.key_hi[b];
+      DIFFKV_CHECK_LENGTHS(a, L, n);
     }
   }
   __device__ __forceinline__ int qtiles(int n) const {
@@ -264,6 +306,7 @@ void split_attn_kernel(const SplitArgs a) {
     n = a.q_lens ? scalar_load(a.q_lens, b) : 1;
     klo = a.key_lo ? scalar_load(a.key_lo, b) : 0;
     khi = a.key_hi ? scalar_load(a.key_hi, b) : INT32_MAX;
+    DIFFKV_CHECK_LENGTHS(a, L, n);
     r0 = -1;                                  // summed below, after the loads are out
   } else {
     SplitPlanner<ROWS> plan(a);
@@ -290,7 +333,7 @@ void split_attn_kernel(const SplitArgs a) {
       if (row) a.part_lse[prow0 + tid] = f32x2{-INFINITY, 0.f};
     } else if (a.part_out) {                  // uniform: whole waves take this branch
       if constexpr (DIRECT) r0 = seq_row_start(a.q_lens, b);
-      if (row) {
+      if (row && DIFFKV_ROW_IN_RANGE(a, r0 + (qt * ROWS + tid) / G)) {
         const int R = qt * ROWS + tid;
         const size_t out_row = (size_t)(r0 + R / G) * a.hq + g * G + R % G;
         for (int d = 0; d < kHeadDimV; d += 4)
@@ -302,7 +345,8 @@ void split_attn_kernel(const SplitArgs a) {
   }
 
   const IO io(a.k_cache, a.v_cache, a.block_table + (size_t)b * a.bt_stride, a.hkv, g,
-              a.log2_page, kv_lo, kv_hi, t_end, WAVE_LOCAL ? lane : tid, WAVE_LOCAL ? 16 * wave : 0);
+              a.log2_page, kv_lo, kv_hi, t_end, WAVE_LOCAL ? lane : tid, WAVE_LOCAL ? 16 * wave : 0,
+              DIFFKV_PAGES(a));
 
   // NS tiles of K/V in flight in registers; page ids NS tiles ahead of the
   // data they address.
@@ -320,7 +364,10 @@ void split_attn_kernel(const SplitArgs a) {
 
   // The query row this lane owns in S^T / O^T.
   const int R = qt * ROWS + rt * 16 + col;
-  const bool row_ok = R < n * G;
+  const bool row_ok = R < n * G && DIFFKV_ROW_IN_RANGE(a, r0 + R / G);
+#ifdef DIFFKV_DEBUG
+  if (qt == 0 && (DIRECT || c == 0)) DIFFKV_CHECK_TOTAL_ROWS(a, b, r0, n);
+#endif
   const int tok = row_ok ? R / G : 0;
   const int h = g * G + (row_ok ? R % G : 0);
   const int p_row = L - n + tok;
@@ -600,10 +647,23 @@ __global__ __launch_bounds__(64 * W) void split_merge_kernel(const SplitArgs a) 
   // are one memory round trip away.  The pair entry is read even for rows
   // past the sequence's own (in bounds: every pair of the launch has one);
   // those rows return before using it.
+#ifdef DIFFKV_DEBUG
+  int n = a.q_lens ? a.q_lens[b] : 1;
+#else
   const int n = a.q_lens ? a.q_lens[b] : 1;
+#endif
   const i32x2 pc = a.pair_chunks[(size_t)b * a.n_qtiles + qt];
   const int r0 = seq_row_start(a.q_lens, b);
+#ifdef DIFFKV_DEBUG
+  {
+    int L = a.seq_lens[b];
+    DIFFKV_CHECK_LENGTHS(a, L, n);
+  }
+#endif
   if (n < a.q_lo || n > a.q_hi || R >= n * G) return;   // uniform over the workgroup
+#ifdef DIFFKV_DEBUG
+  if (!DIFFKV_ROW_IN_RANGE(a, r0 + R / G)) return;      // uniform as well
+#endif
   const int base = pc.x, S = pc.y;
   if (S <= 1) return;                       // written by the split kernel itself
   if (base < 0 || base + S > a.chunk_bound) return;

@@ -42,6 +42,23 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_debug_library_exports_every_declared_symbol():
+    """The debug build (device-side precondition checks) has the same ABI;
+    its flag call rejects a NULL destination before touching the GPU."""
+    path = os.path.join(ROOT, "paged_asymmetric_head_amd", "libdiffkv_attn_debug.so")
+    if not os.path.exists(path):
+        pytest.fail("libdiffkv_attn_debug.so is not built (run __graft_entry__.build())")
+    dlib = ctypes.CDLL(path)
+    for name in declared_functions():
+        assert hasattr(dlib, name), name
+    dlib.diffkv_attn_debug_flags.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert dlib.diffkv_attn_debug_flags(None, None) == B.INVALID_ARGUMENT
+
+
+def test_release_library_has_no_debug_checks(lib):
+    assert lib.diffkv_attn_debug_flags(None, None) == B.UNSUPPORTED
+
+
 def good_desc(**kw):
     d = dict(batch=4, num_q_heads=8, num_kv_heads=1, head_dim_qk=192, head_dim_v=128,
              page_size=128, num_pages=2000, block_table_stride=400, max_seq_len=50000,
