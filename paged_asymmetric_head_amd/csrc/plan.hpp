@@ -116,11 +116,21 @@ inline SplitPlan plan_split(const diffkv_attn_desc& d, int window, int num_cus,
   SplitPlan p;
   const int G = d.num_q_heads / d.num_kv_heads;
   const long long rows_pair = (long long)d.max_q_len * G;
-  p.row_tiles = split_row_tiles((int)(rows_pair < 64 ? rows_pair : 64));
+  const long long max_tiles = ceil_div(max_keys_bound(d, window), kTileKeys) + 1;
+  // Short windows (no pair can hold more than kMinTilesPerSplit tiles, so
+  // one chunk per pair) take 16-row query tiles whatever the rows per pair:
+  // such a launch has few workgroups, each walking its few tiles as a chain
+  // of dependent steps, and 16-row tiles give more workgroups whose waves
+  // each gather and multiply their own keys with no barrier per tile (the
+  // window reads are repeated per query tile, a few MB at most).  On the
+  // sliding-window workloads (64 sequences, 4 new tokens x 8 heads, window
+  // 128, FP8) the call went from 9.4 to 7.8 us (pages of 1) and from 8.5 to
+  // 7.0 us (pages of 128).
+  const bool short_keys = d.force_num_splits <= 0 && max_tiles <= kMinTilesPerSplit;
+  p.row_tiles = short_keys ? 1 : split_row_tiles((int)(rows_pair < 64 ? rows_pair : 64));
   p.rows = 16 * p.row_tiles;
   p.n_qtiles = ceil_div(rows_pair, p.rows);
   const long long pairs = (long long)d.batch * p.n_qtiles;
-  const long long max_tiles = ceil_div(max_keys_bound(d, window), kTileKeys) + 1;
   if (wgs_per_cu == kLaunchSlots)   // bound on the tiles one CU's single chunk would hold
     wgs_per_cu = p.row_tiles == 4 && d.kv_dtype == DIFFKV_KV_BF16 &&
                          pairs * max_tiles * d.num_kv_heads <= (long long)kSlots64MaxTilesPerCu * num_cus
