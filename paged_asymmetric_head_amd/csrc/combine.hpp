@@ -30,20 +30,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;                // whole waves
   const float lse = lane < a.parts ? a.lse_parts[(size_t)lane * a.rows + row] : -INFINITY;
-  float M = lse;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   const float s = a.sinks ? a.sinks[row % a.hq] : -INFINITY;
+  const float M = wave_max_all(lse);
   const float Mt = fmaxf(M, s);
   const float Mu = Mt == -INFINITY ? 0.f : Mt;
   const float w = lse == -INFINITY ? 0.f : fast_exp2((lse - Mu) * kLog2e);
-  float ksum = w;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ksum += __shfl_xor(ksum, o, 64);
+  const float ksum = wave_sum_all(w);
   f32x2 acc = f32x2{0.f, 0.f};
   const float* op = a.out_parts + (size_t)row * kHeadDimV + 2 * lane;
   for (int p = 0; p < a.parts; ++p) {
-    const float wp = __shfl(w, p, 64);
+    const float wp = readlane_f(w, p);
     const f32x2 v = *reinterpret_cast<const f32x2*>(op + (size_t)p * a.rows * kHeadDimV);
     if (wp > 0.f) acc += wp * v;
   }

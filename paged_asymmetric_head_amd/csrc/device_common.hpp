@@ -96,10 +96,6 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
   return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-__device__ __forceinline__ float wave_max_xor(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
-}
-
 // v_max_f32 of two raw registers.  Written out because fmaxf here costs
 // three more instructions: the compiler cannot tell that the row-swap
 // results below are canonical floats, so it re-canonicalises both operands
@@ -126,10 +122,61 @@ __device__ __forceinline__ float max_over_lane_groups(float v) {
   return max_raw(b[0], b[1]);
 }
 
+// Wave-wide scans and reductions on the VALU: DPP row shifts inside each
+// 16-lane row (lanes whose source lies before the row start keep `fill`),
+// then the four row totals read with v_readlane.  A __shfl_xor / __shfl_up
+// ladder compiles to one LDS permute per step, six dependent LDS round trips
+// per ladder, and the split plan runs three ladders before its first K/V
+// load.  The reductions return the same value in every lane.
+template <int N>
+__device__ __forceinline__ int row_shr(int v, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, 0x110 + N, 0xf, 0xf, false);   // DPP row_shr:N
+}
+template <int N>
+__device__ __forceinline__ float row_shr(float v, float fill) {
+  return __builtin_bit_cast(float, row_shr<N>(__builtin_bit_cast(int, v), __builtin_bit_cast(int, fill)));
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_scan_int(int v) {
+  v += row_shr<1>(v, 0);
+  v += row_shr<2>(v, 0);
+  v += row_shr<4>(v, 0);
+  v += row_shr<8>(v, 0);
+  const int t0 = __builtin_amdgcn_readlane(v, 15);
+  const int t1 = __builtin_amdgcn_readlane(v, 31);
+  const int t2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane_id() >> 4;
+  return v + (row > 0 ? t0 : 0) + (row > 1 ? t1 : 0) + (row > 2 ? t2 : 0);
+}
+
 __device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += row_shr<1>(v, 0);
+  v += row_shr<2>(v, 0);
+  v += row_shr<4>(v, 0);
+  v += row_shr<8>(v, 0);
+  return __builtin_amdgcn_readlane(v, 15) + __builtin_amdgcn_readlane(v, 31) +
+         __builtin_amdgcn_readlane(v, 47) + __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+__device__ __forceinline__ float wave_max_all(float v) {
+  v = fmaxf(v, row_shr<1>(v, -INFINITY));
+  v = fmaxf(v, row_shr<2>(v, -INFINITY));
+  v = fmaxf(v, row_shr<4>(v, -INFINITY));
+  v = fmaxf(v, row_shr<8>(v, -INFINITY));
+  return fmaxf(fmaxf(readlane_f(v, 15), readlane_f(v, 31)), fmaxf(readlane_f(v, 47), readlane_f(v, 63)));
+}
+
+__device__ __forceinline__ float wave_sum_all(float v) {
+  v += row_shr<1>(v, 0.f);
+  v += row_shr<2>(v, 0.f);
+  v += row_shr<4>(v, 0.f);
+  v += row_shr<8>(v, 0.f);
+  return (readlane_f(v, 15) + readlane_f(v, 31)) + (readlane_f(v, 47) + readlane_f(v, 63));
 }
 
 // p[i] for a wave-uniform i, as a scalar load through the constant address

@@ -222,14 +222,7 @@ struct SplitPlanner {
       if (b0 > 0) load(b0, L, n, klo, khi);
       // Inclusive prefix sums over the lanes (chunks, and new tokens for the
       // packed row start).
-      auto prefix = [&](int v) {
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(v, o, 64);
-          v += lane_id() >= o ? y : 0;
-        }
-        return v;
-      };
+      auto prefix = [](int v) { return wave_scan_int(v); };
       int kb = seq_chunks(L, n, klo, khi);
       int incl = prefix(kb);
       // One pass holds the whole batch: its count decides whether the
@@ -307,7 +300,11 @@ void split_attn_kernel(const SplitArgs a) {
     klo = a.key_lo ? scalar_load(a.key_lo, b) : 0;
     khi = a.key_hi ? scalar_load(a.key_hi, b) : INT32_MAX;
     DIFFKV_CHECK_LENGTHS(a, L, n);
-    r0 = -1;                                  // summed below, after the loads are out
+    // The packed row start, summed now so that the query rows can be
+    // requested together with the first K/V tile (summed after the tile's
+    // loads, its own loads waited for the tile in the in-order load counter
+    // and put the query rows a round trip behind it).
+    r0 = seq_row_start(a.q_lens, b);
   } else {
     SplitPlanner<ROWS> plan(a);
     plan.init();
@@ -332,7 +329,6 @@ void split_attn_kernel(const SplitArgs a) {
     if (!direct) {
       if (row) a.part_lse[prow0 + tid] = f32x2{-INFINITY, 0.f};
     } else if (a.part_out) {                  // uniform: whole waves take this branch
-      if constexpr (DIRECT) r0 = seq_row_start(a.q_lens, b);
       if (row && DIFFKV_ROW_IN_RANGE(a, r0 + (qt * ROWS + tid) / G)) {
         const int R = qt * ROWS + tid;
         const size_t out_row = (size_t)(r0 + R / G) * a.hq + g * G + R % G;
@@ -349,18 +345,13 @@ void split_attn_kernel(const SplitArgs a) {
               DIFFKV_PAGES(a));
 
   // NS tiles of K/V in flight in registers; page ids NS tiles ahead of the
-  // data they address.
+  // data they address.  Order of the first requests: page ids, query rows
+  // (and the sink), K/V data, so that neither the query rows nor the data
+  // wait for the other.
   typename IO::Pages pg[NS];
   typename IO::Stage st[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) io.fetch_pages(t_begin + i, pg[i]);
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    io.fetch_data(t_begin + i, pg[i], st[i]);
-    io.fetch_pages(t_begin + NS + i, pg[i]);
-  }
-
-  if constexpr (DIRECT) r0 = seq_row_start(a.q_lens, b);
 
   // The query row this lane owns in S^T / O^T.
   const int R = qt * ROWS + rt * 16 + col;
@@ -382,6 +373,15 @@ void split_attn_kernel(const SplitArgs a) {
     for (int c = 0; c < QC; ++c)
       qreg[c] = *reinterpret_cast<const u32x4*>(row_ok ? reinterpret_cast<const uint8_t*>(qp + 32 * c)
                                                        : g_zero_row);
+  }
+  // This row's sink logit, used by a pair of one chunk: loaded here, not
+  // in the epilogue, where it would add a round trip after the last tile.
+  const float sink = *(a.sinks ? a.sinks + h : reinterpret_cast<const float*>(g_zero_row));
+
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    io.fetch_data(t_begin + i, pg[i], st[i]);
+    io.fetch_pages(t_begin + NS + i, pg[i]);
   }
 
   float m = -INFINITY, l = 0.f;
@@ -487,10 +487,16 @@ void split_attn_kernel(const SplitArgs a) {
     l = __builtin_fmaf(l, alpha, psum[0]);
   };
 
-  // Every stage step runs in every round (loads stay in one fixed order, so
-  // the compiler waits for exactly the stage it needs); only the math of
-  // tiles past the split is skipped.
-  for (int t = t_begin; t < t_end; t += NS) {
+  // Every stage step runs in every round that has tiles beyond it (loads
+  // stay in one fixed order, so the compiler waits for exactly the stage it
+  // needs).  The last round issues no look-ahead loads: they would only hold
+  // the waves at their exit (sliding-window verify 7.2 -> 7.0 us).  Page ids
+  // are requested after the tile's products: with large pages they are
+  // scalar loads, which share the LDS reads' completion counter and return
+  // out of order, so a page id requested before the products would make
+  // their first LDS read wait for its whole memory round trip.
+  int t = t_begin;
+  for (; t + NS < t_end; t += NS) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if constexpr (!WAVE_LOCAL) __syncthreads();
@@ -502,9 +508,18 @@ void split_attn_kernel(const SplitArgs a) {
       // 37.5 -> 36.7 us; the shared 32- and 64-row tiles gain nothing).
       if constexpr (WAVE_LOCAL) __builtin_amdgcn_s_setprio(1);
       io.fetch_data(t + i + NS, pg[i], st[i]);
-      io.fetch_pages(t + i + 2 * NS, pg[i]);
       if constexpr (WAVE_LOCAL) __builtin_amdgcn_s_setprio(0);
-      if (t + i < t_end) compute_tile(t + i);
+      compute_tile(t + i);
+      io.fetch_pages(t + i + 2 * NS, pg[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    if (t + i < t_end) {                       // uniform over the workgroup
+      if constexpr (!WAVE_LOCAL) __syncthreads();
+      io.store(st[i], k_lds, v_lds);
+      if constexpr (!WAVE_LOCAL) __syncthreads();
+      compute_tile(t + i);
     }
   }
 
@@ -556,7 +571,7 @@ void split_attn_kernel(const SplitArgs a) {
   if (direct) {
     float coef;
     if (a.sinks) {
-      const float s2 = a.sinks[h] * kLog2e;
+      const float s2 = sink * kLog2e;
       const float M2 = fmaxf(m, s2);
       const float al = fast_exp2(m - M2);
       coef = al / (l * al + fast_exp2(s2 - M2));
@@ -610,16 +625,6 @@ void split_attn_kernel(const SplitArgs a) {
   }
 }
 
-__device__ __forceinline__ float wave_max_all(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum_all(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 
 // Combines the split partials of one query row: weights 2^(lse_s - M) (times
 // 2^e_s on the stored fp16 row), the sink joining the denominator, v_scale,
@@ -642,11 +647,13 @@ __global__ __launch_bounds__(64 * W) void split_merge_kernel(const SplitArgs a) 
   const int bg = blockIdx.y;
   const int b = bg / a.hkv, g = bg % a.hkv;
   const int G = a.group;
-  // The sequence's length, its pair's chunk range and its packed row start
-  // are independent loads: all go out before any is tested, so the partials
-  // are one memory round trip away.  The pair entry is read even for rows
-  // past the sequence's own (in bounds: every pair of the launch has one);
-  // those rows return before using it.
+  // The sequence's length, its pair's chunk range, its packed row start and
+  // the row's sink are independent loads: all go out before any is tested,
+  // so the partials are one memory round trip away and nothing waits on
+  // memory after them.  The pair entry is read even for rows past the
+  // sequence's own (in bounds: every pair of the launch has one); those
+  // rows return before using it.
+  const int tok = R / G, h = g * G + R % G;
 #ifdef DIFFKV_DEBUG
   int n = a.q_lens ? a.q_lens[b] : 1;
 #else
@@ -654,6 +661,7 @@ __global__ __launch_bounds__(64 * W) void split_merge_kernel(const SplitArgs a) 
 #endif
   const i32x2 pc = a.pair_chunks[(size_t)b * a.n_qtiles + qt];
   const int r0 = seq_row_start(a.q_lens, b);
+  const float sink = *(a.sinks ? a.sinks + h : reinterpret_cast<const float*>(g_zero_row));
 #ifdef DIFFKV_DEBUG
   {
     int L = a.seq_lens[b];
@@ -729,8 +737,7 @@ __global__ __launch_bounds__(64 * W) void split_merge_kernel(const SplitArgs a) 
     for (int w = 0; w < W - 1; ++w) acc += red[w][lane];
   }
   ksum = wave_sum_all(ksum);
-  const int tok = R / G, h = g * G + R % G;
-  const float s2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
+  const float s2 = a.sinks ? sink * kLog2e : -INFINITY;
   const float Mt = fmaxf(m_run, s2);
   const float Mt_use = Mt == -INFINITY ? 0.f : Mt;   // a context partial's row with no key
   const float f = fast_exp2(m_run - Mt_use);
