@@ -202,21 +202,30 @@ struct KvTile {
   }
 };
 
+// Rows per new token (the GQA group) as a plain int or a FastDiv.
+__device__ __forceinline__ int group_size(int G) { return G; }
+__device__ __forceinline__ int group_size(const FastDiv& G) { return G.value(); }
+// r / G for r >= -1 (truncating: -1 / G = 0).
+__device__ __forceinline__ int token_of_row(int r, int G) { return r / G; }
+__device__ __forceinline__ int token_of_row(int r, const FastDiv& G) { return r > 0 ? (int)G.div((uint32_t)r) : 0; }
+
 // Keys one block of query rows can see: the union of its rows' ranges.
 // Row r of a (sequence, KV head) is new token r / G.
-__device__ __forceinline__ void qtile_key_range(int L, int n, int G, int qt, int rows, int window,
+template <class Group>
+__device__ __forceinline__ void qtile_key_range(int L, int n, const Group& G, int qt, int rows, int window,
                                                 int& kv_lo, int& kv_hi) {
   const int r_lo = qt * rows;
-  const int r_hi = min(n * G, r_lo + rows) - 1;
-  const int p_lo = L - n + r_lo / G;
-  const int p_hi = L - n + r_hi / G;
+  const int r_hi = min(n * group_size(G), r_lo + rows) - 1;
+  const int p_lo = L - n + token_of_row(r_lo, G);
+  const int p_hi = L - n + token_of_row(r_hi, G);
   kv_lo = window > 0 ? max(0, p_lo - window + 1) : 0;
   kv_hi = p_hi + 1;
 }
 
 // The same range cut to the keys [klo, khi) (a context partial's share); it
 // may come out empty (hi <= lo).
-__device__ __forceinline__ void pair_key_range(int L, int n, int G, int qt, int rows, int window,
+template <class Group>
+__device__ __forceinline__ void pair_key_range(int L, int n, const Group& G, int qt, int rows, int window,
                                                int klo, int khi, int& kv_lo, int& kv_hi) {
   qtile_key_range(L, n, G, qt, rows, window, kv_lo, kv_hi);
   kv_lo = max(kv_lo, klo);

@@ -133,11 +133,17 @@ __device__ __forceinline__ void split_tiles(int kv_lo, int kv_hi, int S, int s, 
 template <int ROWS>
 struct SplitPlanner {
   const SplitArgs& a;
+  const FastDiv& G;     // the GQA group
   int C = 0;            // tiles per chunk; 0 with forced splits
+  FastDiv Cd{1};        // division by C (set with C)
   int L0 = 0, n0 = 0;   // this lane's sequence (b = lane) of the first pass
   int lo0 = 0, hi0 = 0; // its key bounds
 
-  __device__ __forceinline__ explicit SplitPlanner(const SplitArgs& args) : a(args) {}
+  __device__ __forceinline__ SplitPlanner(const SplitArgs& args, const FastDiv& group) : a(args), G(group) {}
+  __device__ __forceinline__ void set_chunk(int c) {
+    C = c;
+    Cd = FastDiv((uint32_t)c);
+  }
 
   // Lengths and key bounds of sequence b0 + lane (new tokens 0 past the batch).
   __device__ __forceinline__ void load(int b0, int& L, int& n, int& klo, int& khi) const {
@@ -155,17 +161,17 @@ struct SplitPlanner {
     }
   }
   __device__ __forceinline__ int qtiles(int n) const {
-    return n >= a.q_lo && n <= a.q_hi ? min((n * a.group + ROWS - 1) / ROWS, a.n_qtiles) : 0;
+    return n >= a.q_lo && n <= a.q_hi ? min((n * G.value() + ROWS - 1) / ROWS, a.n_qtiles) : 0;
   }
   __device__ __forceinline__ int tiles(int L, int n, int qt, int klo, int khi) const {
     int lo, hi;
-    pair_key_range(L, n, a.group, qt, ROWS, a.window, klo, khi, lo, hi);
+    pair_key_range(L, n, G, qt, ROWS, a.window, klo, khi, lo, hi);
     return hi > lo ? (hi + kTileKeys - 1) / kTileKeys - lo / kTileKeys : 0;
   }
   // At least one chunk per pair, so a pair with no key in range still
   // writes its rows.
   __device__ __forceinline__ int chunks(int L, int n, int qt, int klo, int khi) const {
-    return a.force_splits > 0 ? a.force_splits : max(1, (tiles(L, n, qt, klo, khi) + C - 1) / C);
+    return a.force_splits > 0 ? a.force_splits : max(1, (int)Cd.div((uint32_t)(tiles(L, n, qt, klo, khi) + C - 1)));
   }
   // Chunks of all query tiles of a sequence (0 for one this launch skips).
   __device__ __forceinline__ int seq_chunks(int L, int n, int klo, int khi) const {
@@ -186,7 +192,7 @@ struct SplitPlanner {
       for (int qt = 0; qt < nq; ++qt) T += tiles(L, n, qt, klo, khi);
     }
     T = wave_sum_int(T);
-    C = max(kMinTilesPerSplit, (T + a.slots - 1) / a.slots);
+    set_chunk(max(kMinTilesPerSplit, (T + a.slots - 1) / a.slots));
     // Rounding every pair up to whole chunks can give more chunks than the
     // slots of one resident round (up to slots + pairs, which the grid
     // covers); the chunks past the round would start only when others end
@@ -196,7 +202,7 @@ struct SplitPlanner {
     // Up to 64 sequences the check rides on find()'s own prefix sum, which
     // already counts every chunk; larger batches count here.
     if (a.batch > 64)
-      for (int it = 0; it < kFitSteps && total_chunks() > a.slots; ++it) C += max(1, C >> 5);
+      for (int it = 0; it < kFitSteps && total_chunks() > a.slots; ++it) set_chunk(C + max(1, C >> 5));
   }
   static constexpr int kFitSteps = 8;
 
@@ -229,7 +235,7 @@ struct SplitPlanner {
       // chunks fit one resident round (see init).
       if (a.batch <= 64 && a.force_splits <= 0) {
         for (int it = 0; it < kFitSteps && read_lane(incl, 63) > a.slots; ++it) {
-          C += max(1, C >> 5);
+          set_chunk(C + max(1, C >> 5));
           kb = seq_chunks(L, n, klo, khi);
           incl = prefix(kb);
         }
@@ -288,6 +294,7 @@ void split_attn_kernel(const SplitArgs a) {
   const int rt = wave % RT, kg = wave / RT;
   const int g = blockIdx.y;
   const int G = a.group;
+  const FastDiv gdiv((uint32_t)G);
 
   // Which pair and chunk: one chunk per pair when DIRECT (grid.x = pairs),
   // else the balanced plan.
@@ -306,7 +313,7 @@ void split_attn_kernel(const SplitArgs a) {
     // and put the query rows a round trip behind it).
     r0 = seq_row_start(a.q_lens, b);
   } else {
-    SplitPlanner<ROWS> plan(a);
+    SplitPlanner<ROWS> plan(a, gdiv);
     plan.init();
     if (!plan.find(blockIdx.x, b, qt, c, base, k, L, n, klo, khi, r0) || base + c >= a.chunk_bound)
       return;
@@ -317,7 +324,7 @@ void split_attn_kernel(const SplitArgs a) {
   // A pair of one chunk writes its output here; the merge skips it.
   const bool direct = DIRECT || k == 1;
   int kv_lo, kv_hi, t_begin = 0, t_end = 0;
-  pair_key_range(L, n, G, qt, ROWS, a.window, klo, khi, kv_lo, kv_hi);
+  pair_key_range(L, n, gdiv, qt, ROWS, a.window, klo, khi, kv_lo, kv_hi);
   if (kv_hi > kv_lo) split_tiles(kv_lo, kv_hi, k, c, t_begin, t_end);
   // Partial row of this chunk for row r of the tile.
   const size_t prow0 = ((size_t)(base + c) * a.hkv + g) * ROWS;
@@ -359,8 +366,8 @@ void split_attn_kernel(const SplitArgs a) {
 #ifdef DIFFKV_DEBUG
   if (qt == 0 && (DIRECT || c == 0)) DIFFKV_CHECK_TOTAL_ROWS(a, b, r0, n);
 #endif
-  const int tok = row_ok ? R / G : 0;
-  const int h = g * G + (row_ok ? R % G : 0);
+  const int tok = row_ok ? (int)gdiv.div((uint32_t)R) : 0;
+  const int h = g * G + (row_ok ? R - tok * G : 0);
   const int p_row = L - n + tok;
   const int lo_row = max(a.window > 0 ? max(0, p_row - a.window + 1) : 0, klo);
   const int hi_row = row_ok ? min(p_row, khi - 1) : -1;   // empty interval for padding rows
@@ -396,8 +403,8 @@ void split_attn_kernel(const SplitArgs a) {
   // results stay in their own lanes and are never written.
   const int r_first = qt * ROWS;
   const int r_last = min(n * G, r_first + ROWS) - 1;
-  const int p_first = min(L - n + r_first / G, khi - 1);
-  const int lo_last = max(a.window > 0 ? max(0, L - n + r_last / G - a.window + 1) : 0, klo);
+  const int p_first = min(L - n + token_of_row(r_first, gdiv), khi - 1);
+  const int lo_last = max(a.window > 0 ? max(0, L - n + token_of_row(r_last, gdiv) - a.window + 1) : 0, klo);
   const float scale = a.scale_log2;   // > 0 (checked on the host)
 
   // One online-softmax update per tile: the S^T tiles of all this wave's
