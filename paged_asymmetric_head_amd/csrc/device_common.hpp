@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+#include "fast_div.hpp"
+
 namespace diffkv {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -19,26 +21,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
-// Unsigned division by a divisor fixed for a launch (the GQA group, the
-// split plan's chunk length): a multiply-high by m = floor((2^32 - 1) / d)
-// and at most two corrections, exact for every 32-bit dividend (m * x / 2^32
-// lies in (x / d - 2, x / d]).  The plan divides per lane before its first
-// K/V load; the compiler's general sequence there (a reciprocal, a
-// multiply-high and two corrections, with the reciprocal rebuilt for every
-// division) sits on that path.
-struct FastDiv {
-  uint32_t d, m;
-  __device__ __forceinline__ explicit FastDiv(uint32_t divisor) : d(divisor), m(0xffffffffu / divisor) {}
-  __device__ __forceinline__ uint32_t div(uint32_t x) const {
-    uint32_t q = __umulhi(x, m);
-    uint32_t r = x - q * d;
-    if (r >= d) { ++q; r -= d; }
-    if (r >= d) ++q;
-    return q;
-  }
-  __device__ __forceinline__ int value() const { return (int)d; }
-};
 
 // S/O tiles: D(16x16, fp32) += A(16 x K) * B(K x 16) on the matrix cores.
 // Operand layout shared by both shapes: lane l supplies row (l % 16) of A and

@@ -9,12 +9,18 @@
 //   scale                 the planner's grid, workspace and one-resident-round
 //                         bound at 32, 80 and 256 CUs for the decode and verify
 //                         workloads' shapes
+//   fastdiv               the kernels' multiply-high division (fast_div.hpp)
+//                         against the division operator: every dividend below
+//                         2^16 for divisors 1..1024, dividends at and around
+//                         multiples of the divisor and at the top of the range,
+//                         and seeded random (dividend, divisor) pairs
 // Exits 0 when every check holds; prints the first failure and exits 1.
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 
+#include "fast_div.hpp"
 #include "plan.hpp"
 #include "validate.hpp"
 
@@ -181,6 +187,32 @@ int scale() {
 
 }  // namespace
 
+int fastdiv() {
+  long checked = 0;
+  auto one = [&](uint32_t x, uint32_t d) {
+    ++checked;
+    const uint32_t got = FastDiv(d).div(x), want = x / d;
+    if (got != want && !g_fail) {
+      g_fail = 1;
+      std::printf("FAIL fastdiv: %u / %u = %u, got %u\n", x, d, want, got);
+    }
+  };
+  for (uint32_t d = 1; d <= 1024 && !g_fail; ++d)
+    for (uint32_t x = 0; x < 65536u; ++x) one(x, d);
+  Rng rng{12345};
+  for (int i = 0; i < 200000 && !g_fail; ++i) {
+    uint32_t d = (uint32_t)rng.next();
+    if (i % 3 == 0) d >>= (uint32_t)(rng.next() % 32);
+    if (d == 0) d = 1;
+    const uint32_t q = 0xffffffffu / d;
+    const uint32_t edges[] = {0u, 1u, d - 1, d, d + 1, q * d, q * d - 1, 0xffffffffu, 0xfffffffeu,
+                              (uint32_t)rng.next()};
+    for (uint32_t x : edges) one(x, d);
+  }
+  std::printf("fastdiv: %ld (dividend, divisor) pairs\n", checked);
+  return g_fail;
+}
+
 int main(int argc, char** argv) {
   if (argc >= 2 && std::strcmp(argv[1], "fuzz") == 0) {
     const uint64_t seed = argc >= 3 ? std::strtoull(argv[2], nullptr, 10) : 1;
@@ -188,6 +220,7 @@ int main(int argc, char** argv) {
     return fuzz(seed, count);
   }
   if (argc >= 2 && std::strcmp(argv[1], "scale") == 0) return scale();
-  std::printf("usage: %s fuzz <seed> <count> | scale\n", argv[0]);
+  if (argc >= 2 && std::strcmp(argv[1], "fastdiv") == 0) return fastdiv();
+  std::printf("usage: %s fuzz <seed> <count> | scale | fastdiv\n", argv[0]);
   return 2;
 }

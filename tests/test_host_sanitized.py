@@ -51,3 +51,7 @@ def test_descriptor_fuzz_under_sanitizers(host_check, seed):
 
 def test_plan_scales_with_compute_units(host_check):
     run(host_check, "scale")
+
+
+def test_multiply_high_division_is_exact(host_check):
+    run(host_check, "fastdiv")
