@@ -270,6 +270,166 @@ struct SplitPlanner {
   }
 };
 
+// Short key ranges: a pair whose keys span at most kWinTiles 64-key tiles
+// (a sliding window of a few hundred keys, a short sequence) in a launch of
+// one workgroup per pair with 16-row query tiles.  Every tile's loads go out
+// at once and each wave runs one softmax update over all of them, instead of
+// a chain of dependent per-tile steps, each waiting for its own tile.  Wave w
+// takes keys 16w .. 16w+15 of every tile, as the wave-local loop does.  K
+// goes from memory straight into the MFMA operand registers: lane group grp
+// holds the contiguous dims DQK/4 * grp .. + DQK/4 of the lane's key, and the
+// query rows are loaded with the same assignment of dims to contraction
+// steps (S^T = K Q^T only needs both operands to agree), so K makes no LDS
+// round trip.  V goes through LDS for the transposing reads, one region per
+// tile.  Slots past the pair's last tile, and keys outside [kv_lo, kv_hi),
+// read the zero row; the row masks drop every key a row does not see.
+constexpr int kWinTiles = 4;
+
+template <bool FP8, bool UPAGE, bool COUNT, int DQK>
+__device__ __forceinline__ void window_pass(const SplitArgs& a, int b, int g, int kv_lo, int kv_hi,
+                                            int t_begin, int t_end, int wave, int lane,
+                                            const uint16_t* q_row, bool row_ok, int lo_row, int hi_row,
+                                            uint16_t* v_lds, float& m, float& l, f32x4 (&o)[8], int& cnt) {
+  constexpr int ESZ = FP8 ? 1 : 2;
+  constexpr int QC = DQK / 32;             // contraction steps of 8 dims per lane
+  constexpr int KD = DQK / 4;              // dims of a K row per lane group
+  constexpr int KL = KD * ESZ / 16;        // 16-byte K loads per lane and tile
+  constexpr int VL = 32 * ESZ / 16;        // 16-byte V loads per lane and tile (32 dims)
+  const int col = lane & 15, grp = lane >> 4;
+  const uint8_t* k_head = a.k_cache + (size_t)g * DQK * ESZ;
+  const uint8_t* v_head = a.v_cache + (size_t)g * kHeadDimV * ESZ;
+  const size_t k_slot = (size_t)a.hkv * DQK * ESZ, v_slot = (size_t)a.hkv * kHeadDimV * ESZ;
+  const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
+  const int lp = a.log2_page, pmask = (1 << lp) - 1;
+  const int nt = t_end - t_begin;
+  // Keys this lane loads: K row (the lane's column of the K fragment) and
+  // V piece (16 keys x 4 pieces of 32 dims).
+  const int k_key = 16 * wave + col, v_key = 16 * wave + (lane >> 2), v_piece = lane & 3;
+  auto readable = [&](int i, int j) { return i < nt && j >= kv_lo && j < kv_hi; };
+
+  int pk[kWinTiles], pv[kWinTiles];
+#pragma unroll
+  for (int i = 0; i < kWinTiles; ++i) {
+    const int t = min(t_begin + i, t_end - 1);
+    if constexpr (UPAGE) {
+      pk[i] = scalar_load(bt, (t * kTileKeys) >> lp);   // a tile lies inside one page
+      pv[i] = pk[i];
+    } else {
+      const int jk = (t_begin + i) * kTileKeys + k_key, jv = (t_begin + i) * kTileKeys + v_key;
+      pk[i] = bt[(readable(i, jk) ? jk : kv_lo) >> lp];
+      pv[i] = bt[(readable(i, jv) ? jv : kv_lo) >> lp];
+    }
+#ifdef DIFFKV_DEBUG
+    if ((unsigned)pk[i] >= (unsigned)a.num_pages || (unsigned)pv[i] >= (unsigned)a.num_pages) {
+      debug_flag(kDbgPage);
+      pk[i] = 0;
+      pv[i] = 0;
+    }
+#endif
+  }
+  // Query rows: step c carries dims KD * grp + 8c .. + 7.
+  u32x4 qreg[QC];
+#pragma unroll
+  for (int c = 0; c < QC; ++c)
+    qreg[c] = *reinterpret_cast<const u32x4*>(row_ok ? reinterpret_cast<const uint8_t*>(q_row + KD * grp + 8 * c)
+                                                     : g_zero_row);
+  // Every K load, then every V load: the products wait for K alone (loads
+  // complete in issue order), and V arrives while QK^T and the softmax run.
+  u32x4 kr[kWinTiles][KL], vr[kWinTiles][VL];
+#pragma unroll
+  for (int i = 0; i < kWinTiles; ++i) {
+    const int jk = (t_begin + i) * kTileKeys + k_key;
+    const uint8_t* kp = k_head + (((size_t)pk[i] << lp) | (size_t)(jk & pmask)) * k_slot + KD * grp * ESZ;
+    const bool rk = readable(i, jk);
+#pragma unroll
+    for (int u = 0; u < KL; ++u) kr[i][u] = *reinterpret_cast<const u32x4*>(rk ? kp + 16 * u : g_zero_row);
+  }
+#pragma unroll
+  for (int i = 0; i < kWinTiles; ++i) {
+    const int jv = (t_begin + i) * kTileKeys + v_key;
+    const uint8_t* vp = v_head + (((size_t)pv[i] << lp) | (size_t)(jv & pmask)) * v_slot + 32 * v_piece * ESZ;
+    const bool rv = readable(i, jv);
+#pragma unroll
+    for (int u = 0; u < VL; ++u) vr[i][u] = *reinterpret_cast<const u32x4*>(rv ? vp + 16 * u : g_zero_row);
+  }
+
+  // S^T of every tile: independent MFMA chains.
+  f32x4 sacc[kWinTiles];
+#pragma unroll
+  for (int i = 0; i < kWinTiles; ++i) sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < QC; ++c)
+#pragma unroll
+    for (int i = 0; i < kWinTiles; ++i) {
+      u32x4 kf;
+      if constexpr (FP8) {
+        const uint32_t w0 = (c & 1) ? kr[i][c >> 1].z : kr[i][c >> 1].x;
+        const uint32_t w1 = (c & 1) ? kr[i][c >> 1].w : kr[i][c >> 1].y;
+        kf = cat(e4m3x4_to_bf16x4(w0), e4m3x4_to_bf16x4(w1));
+      } else {
+        kf = kr[i][c];
+      }
+      sacc[i] = mfma_16x16x32(kf, qreg[c], sacc[i]);
+    }
+
+  // sacc[i][r] = raw score of key (t_begin + i) * 64 + 16 wave + 4 grp + r.
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kWinTiles; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = (t_begin + i) * kTileKeys + 16 * wave + 4 * grp + r;
+      const bool vis = j >= lo_row && j <= hi_row;
+      sacc[i][r] = vis ? sacc[i][r] : -INFINITY;
+      if constexpr (COUNT) cnt += vis ? 1 : 0;
+      mx = fmaxf(mx, sacc[i][r]);
+    }
+  mx = max_over_lane_groups(mx);
+  const float scale = a.scale_log2;
+  m = next_reference(-INFINITY, mx * scale);
+  const float m_use = m == -INFINITY ? 0.f : m;
+  u32x2 pb[kWinTiles];
+#pragma unroll
+  for (int i = 0; i < kWinTiles; ++i) {
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(__builtin_fmaf(sacc[i][r], scale, -m_use));
+    pb[i] = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+  }
+
+  // V rows into LDS (bf16, row-major), this wave's 16 rows of each tile's
+  // region; only this wave reads them, so program order suffices.
+#pragma unroll
+  for (int i = 0; i < kWinTiles; ++i) {
+    uint16_t* dst = v_lds + i * kVLdsElems + v_key * kVLdsStride + 32 * v_piece;
+#pragma unroll
+    for (int u = 0; u < VL; ++u) {
+      if constexpr (FP8) {
+        const u32x2 c0 = e4m3x4_to_bf16x4(vr[i][u].x), c1 = e4m3x4_to_bf16x4(vr[i][u].y);
+        const u32x2 c2 = e4m3x4_to_bf16x4(vr[i][u].z), c3 = e4m3x4_to_bf16x4(vr[i][u].w);
+        *reinterpret_cast<u32x4*>(dst + 16 * u) = u32x4{c0.x, c0.y, c1.x, c1.y};
+        *reinterpret_cast<u32x4*>(dst + 16 * u + 8) = u32x4{c2.x, c2.y, c3.x, c3.y};
+      } else {
+        *reinterpret_cast<u32x4*>(dst + 8 * u) = vr[i][u];
+      }
+    }
+  }
+
+  // O^T = V^T P^T over two tiles' 16 keys per step (32 keys, as the loop's
+  // paired subtiles), the row sums from the all-ones tile.
+  f32x4 psum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kWinTiles; i += 2) {
+    const u32x4 pt = cat(pb[i], pb[i + 1]);
+    const uint16_t* vp = v_lds + i * kVLdsElems + (16 * wave + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn)
+      o[nn] = mfma_16x16x32(cat(lds_read_tr16(vp + 16 * nn), lds_read_tr16(vp + kVLdsElems + 16 * nn)), pt, o[nn]);
+    psum = mfma_16x16x32(kOnesBf16x8, pt, psum);
+  }
+  l = psum[0];
+}
+
 template <bool FP8, int RT, bool DIRECT, bool COUNT, bool UPAGE, int NS, int DQK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSplitWavesPerEu, 8)))
 void split_attn_kernel(const SplitArgs a) {
@@ -284,7 +444,12 @@ void split_attn_kernel(const SplitArgs a) {
   // and gather the tile together, with barriers.
   constexpr bool WAVE_LOCAL = RT == 1;
   using IO = std::conditional_t<WAVE_LOCAL, KvTile<FP8, UPAGE, DQK, 64, 16>, KvTile<FP8, UPAGE, DQK>>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kKLdsElems<DQK> + kVLdsElems];
+  // One K/V tile, or, for the short-range pass of one-chunk launches, the V
+  // regions of kWinTiles tiles.
+  constexpr int LDS_ELEMS = DIRECT && WAVE_LOCAL && kWinTiles * kVLdsElems > kKLdsElems<DQK> + kVLdsElems
+                                ? kWinTiles * kVLdsElems
+                                : kKLdsElems<DQK> + kVLdsElems;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
   uint16_t* k_lds = lds;
   uint16_t* v_lds = lds + kKLdsElems<DQK>;
 
@@ -347,19 +512,6 @@ void split_attn_kernel(const SplitArgs a) {
     return;
   }
 
-  const IO io(a.k_cache, a.v_cache, a.block_table + (size_t)b * a.bt_stride, a.hkv, g,
-              a.log2_page, kv_lo, kv_hi, t_end, WAVE_LOCAL ? lane : tid, WAVE_LOCAL ? 16 * wave : 0,
-              DIFFKV_PAGES(a));
-
-  // NS tiles of K/V in flight in registers; page ids NS tiles ahead of the
-  // data they address.  Order of the first requests: page ids, query rows
-  // (and the sink), K/V data, so that neither the query rows nor the data
-  // wait for the other.
-  typename IO::Pages pg[NS];
-  typename IO::Stage st[NS];
-#pragma unroll
-  for (int i = 0; i < NS; ++i) io.fetch_pages(t_begin + i, pg[i]);
-
   // The query row this lane owns in S^T / O^T.
   const int R = qt * ROWS + rt * 16 + col;
   const bool row_ok = R < n * G && DIFFKV_ROW_IN_RANGE(a, r0 + R / G);
@@ -372,24 +524,9 @@ void split_attn_kernel(const SplitArgs a) {
   const int lo_row = max(a.window > 0 ? max(0, p_row - a.window + 1) : 0, klo);
   const int hi_row = row_ok ? min(p_row, khi - 1) : -1;   // empty interval for padding rows
 
-  // Q^T operand: contraction chunk c carries dims 32c + 8*grp .. +7.
-  u32x4 qreg[QC];
-  {
-    const uint16_t* qp = a.q + ((size_t)(r0 + tok) * a.hq + h) * DQK + 8 * grp;
-#pragma unroll
-    for (int c = 0; c < QC; ++c)
-      qreg[c] = *reinterpret_cast<const u32x4*>(row_ok ? reinterpret_cast<const uint8_t*>(qp + 32 * c)
-                                                       : g_zero_row);
-  }
   // This row's sink logit, used by a pair of one chunk: loaded here, not
   // in the epilogue, where it would add a round trip after the last tile.
   const float sink = *(a.sinks ? a.sinks + h : reinterpret_cast<const float*>(g_zero_row));
-
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    io.fetch_data(t_begin + i, pg[i], st[i]);
-    io.fetch_pages(t_begin + NS + i, pg[i]);
-  }
 
   float m = -INFINITY, l = 0.f;
   f32x4 o[8];
@@ -397,136 +534,172 @@ void split_attn_kernel(const SplitArgs a) {
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   int cnt = 0;
 
-  // Tiles every row of the workgroup sees whole (no key past the first row's
-  // position, none before the last row's window start) skip the mask.
-  // Padding rows past n*G may then score keys they would not see; their
-  // results stay in their own lanes and are never written.
-  const int r_first = qt * ROWS;
-  const int r_last = min(n * G, r_first + ROWS) - 1;
-  const int p_first = min(L - n + token_of_row(r_first, gdiv), khi - 1);
-  const int lo_last = max(a.window > 0 ? max(0, L - n + token_of_row(r_last, gdiv) - a.window + 1) : 0, klo);
-  const float scale = a.scale_log2;   // > 0 (checked on the host)
+  bool windowed = false;
+  if constexpr (DIRECT && WAVE_LOCAL) windowed = t_end - t_begin <= kWinTiles;   // uniform
+  if (windowed) {
+    window_pass<FP8, UPAGE, COUNT, DQK>(a, b, g, kv_lo, kv_hi, t_begin, t_end, wave, lane,
+                                        a.q + ((size_t)(r0 + tok) * a.hq + h) * DQK, row_ok, lo_row,
+                                        hi_row, lds, m, l, o, cnt);
+  } else {
+    const IO io(a.k_cache, a.v_cache, a.block_table + (size_t)b * a.bt_stride, a.hkv, g,
+                a.log2_page, kv_lo, kv_hi, t_end, WAVE_LOCAL ? lane : tid, WAVE_LOCAL ? 16 * wave : 0,
+                DIFFKV_PAGES(a));
 
-  // One online-softmax update per tile: the S^T tiles of all this wave's
-  // 16-key subtiles first (independent MFMA chains), one max / rescale / sum
-  // over them, then all the P*V products.
-  auto compute_tile = [&](int t) {
-    f32x4 sacc[SUBS];
+    // NS tiles of K/V in flight in registers; page ids NS tiles ahead of the
+    // data they address.  Order of the first requests: (the sink,) page ids,
+    // query rows, K/V data, so that neither the query rows nor the data wait
+    // for the other.
+    typename IO::Pages pg[NS];
+    typename IO::Stage st[NS];
 #pragma unroll
-    for (int sub = 0; sub < SUBS; ++sub) sacc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NS; ++i) io.fetch_pages(t_begin + i, pg[i]);
+
+    // Q^T operand: contraction chunk c carries dims 32c + 8*grp .. +7.
+    u32x4 qreg[QC];
+    {
+      const uint16_t* qp = a.q + ((size_t)(r0 + tok) * a.hq + h) * DQK + 8 * grp;
 #pragma unroll
-    for (int c = 0; c < QC; ++c)
+      for (int c = 0; c < QC; ++c)
+        qreg[c] = *reinterpret_cast<const u32x4*>(row_ok ? reinterpret_cast<const uint8_t*>(qp + 32 * c)
+                                                         : g_zero_row);
+    }
 #pragma unroll
-      for (int sub = 0; sub < SUBS; ++sub) {
-        const uint16_t* kp = k_lds + ((kg * SUBS + sub) * 16 + col) * kKLdsStride<DQK> + 8 * grp + 32 * c;
-        sacc[sub] = mfma_16x16x32(*reinterpret_cast<const u32x4*>(kp), qreg[c], sacc[sub]);
+    for (int i = 0; i < NS; ++i) {
+      io.fetch_data(t_begin + i, pg[i], st[i]);
+      io.fetch_pages(t_begin + NS + i, pg[i]);
+    }
+
+    // Tiles every row of the workgroup sees whole (no key past the first row's
+    // position, none before the last row's window start) skip the mask.
+    // Padding rows past n*G may then score keys they would not see; their
+    // results stay in their own lanes and are never written.
+    const int r_first = qt * ROWS;
+    const int r_last = min(n * G, r_first + ROWS) - 1;
+    const int p_first = min(L - n + token_of_row(r_first, gdiv), khi - 1);
+    const int lo_last = max(a.window > 0 ? max(0, L - n + token_of_row(r_last, gdiv) - a.window + 1) : 0, klo);
+    const float scale = a.scale_log2;   // > 0 (checked on the host)
+
+    // One online-softmax update per tile: the S^T tiles of all this wave's
+    // 16-key subtiles first (independent MFMA chains), one max / rescale / sum
+    // over them, then all the P*V products.
+    auto compute_tile = [&](int t) {
+      f32x4 sacc[SUBS];
+#pragma unroll
+      for (int sub = 0; sub < SUBS; ++sub) sacc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < QC; ++c)
+#pragma unroll
+        for (int sub = 0; sub < SUBS; ++sub) {
+          const uint16_t* kp = k_lds + ((kg * SUBS + sub) * 16 + col) * kKLdsStride<DQK> + 8 * grp + 32 * c;
+          sacc[sub] = mfma_16x16x32(*reinterpret_cast<const u32x4*>(kp), qreg[c], sacc[sub]);
+        }
+
+      // sacc[sub][i] = raw S^T[key (kg*SUBS+sub)*16 + 4*grp + i][row col].
+      // The branch is uniform over the workgroup.
+      if (t * kTileKeys < lo_last || t * kTileKeys + kTileKeys - 1 > p_first) {
+#pragma unroll
+        for (int sub = 0; sub < SUBS; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = t * kTileKeys + (kg * SUBS + sub) * 16 + 4 * grp + i;
+            const bool vis = j >= lo_row && j <= hi_row;
+            sacc[sub][i] = vis ? sacc[sub][i] : -INFINITY;
+            if constexpr (COUNT) cnt += vis ? 1 : 0;
+          }
+      } else {
+        if constexpr (COUNT) cnt += 4 * SUBS;
       }
-
-    // sacc[sub][i] = raw S^T[key (kg*SUBS+sub)*16 + 4*grp + i][row col].
-    // The branch is uniform over the workgroup.
-    if (t * kTileKeys < lo_last || t * kTileKeys + kTileKeys - 1 > p_first) {
+      float mx = -INFINITY;
 #pragma unroll
       for (int sub = 0; sub < SUBS; ++sub)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = t * kTileKeys + (kg * SUBS + sub) * 16 + 4 * grp + i;
-          const bool vis = j >= lo_row && j <= hi_row;
-          sacc[sub][i] = vis ? sacc[sub][i] : -INFINITY;
-          if constexpr (COUNT) cnt += vis ? 1 : 0;
-        }
-    } else {
-      if constexpr (COUNT) cnt += 4 * SUBS;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < SUBS; ++sub)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[sub][i]);
-    mx = max_over_lane_groups(mx);
-    const float m_new = next_reference(m, mx * scale);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    u32x2 pb[SUBS];
-#pragma unroll
-    for (int sub = 0; sub < SUBS; ++sub) {
-      float pr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(__builtin_fmaf(sacc[sub][i], scale, -m_use));
-      pb[sub] = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
-    }
-    m = m_new;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int nn = 0; nn < 8; ++nn) o[nn] *= alpha;
-    }
-
-    // V^T operand straight from the row-major tile: in each 16-lane group the
-    // transposing read hands lane col the dim 16*nn + col of keys
-    // 4*grp + 0..3 when source lane col reads 4 dims (16*nn + 4*(col%4))
-    // of key 4*grp + col/4.  The row sums of the (bf16) P come from an extra
-    // all-ones V^T tile: every element of psum is sum_k P[row][k].
-    // With two or more subtiles per wave the products contract 32 keys at a
-    // time: lane group grp takes keys 4grp + 0..3 of subtiles 2c and 2c+1 (the
-    // P values it holds), and two transposing reads give the matching V^T.
-    f32x4 psum = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (SUBS % 2 == 0) {
-#pragma unroll
-      for (int c = 0; c < SUBS / 2; ++c) {
-        const u32x4 pt = cat(pb[2 * c], pb[2 * c + 1]);
-        const uint16_t* vp =
-            v_lds + ((kg * SUBS + 2 * c) * 16 + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
-#pragma unroll
-        for (int nn = 0; nn < 8; ++nn)
-          o[nn] = mfma_16x16x32(cat(lds_read_tr16(vp + 16 * nn), lds_read_tr16(vp + 16 * kVLdsStride + 16 * nn)),
-                                pt, o[nn]);
-        psum = mfma_16x16x32(kOnesBf16x8, pt, psum);
-      }
-    } else {
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[sub][i]);
+      mx = max_over_lane_groups(mx);
+      const float m_new = next_reference(m, mx * scale);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m - m_use);
+      u32x2 pb[SUBS];
 #pragma unroll
       for (int sub = 0; sub < SUBS; ++sub) {
-        const uint16_t* vp = v_lds + ((kg * SUBS + sub) * 16 + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
+        float pr[4];
 #pragma unroll
-        for (int nn = 0; nn < 8; ++nn)
-          o[nn] = mfma_16x16x16(lds_read_tr16(vp + 16 * nn), pb[sub], o[nn]);
-        psum = mfma_16x16x16(kOnesBf16x4, pb[sub], psum);
+        for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(__builtin_fmaf(sacc[sub][i], scale, -m_use));
+        pb[sub] = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+      }
+      m = m_new;
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn) o[nn] *= alpha;
+      }
+
+      // V^T operand straight from the row-major tile: in each 16-lane group the
+      // transposing read hands lane col the dim 16*nn + col of keys
+      // 4*grp + 0..3 when source lane col reads 4 dims (16*nn + 4*(col%4))
+      // of key 4*grp + col/4.  The row sums of the (bf16) P come from an extra
+      // all-ones V^T tile: every element of psum is sum_k P[row][k].
+      // With two or more subtiles per wave the products contract 32 keys at a
+      // time: lane group grp takes keys 4grp + 0..3 of subtiles 2c and 2c+1 (the
+      // P values it holds), and two transposing reads give the matching V^T.
+      f32x4 psum = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (SUBS % 2 == 0) {
+#pragma unroll
+        for (int c = 0; c < SUBS / 2; ++c) {
+          const u32x4 pt = cat(pb[2 * c], pb[2 * c + 1]);
+          const uint16_t* vp =
+              v_lds + ((kg * SUBS + 2 * c) * 16 + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
+#pragma unroll
+          for (int nn = 0; nn < 8; ++nn)
+            o[nn] = mfma_16x16x32(cat(lds_read_tr16(vp + 16 * nn), lds_read_tr16(vp + 16 * kVLdsStride + 16 * nn)),
+                                  pt, o[nn]);
+          psum = mfma_16x16x32(kOnesBf16x8, pt, psum);
+        }
+      } else {
+#pragma unroll
+        for (int sub = 0; sub < SUBS; ++sub) {
+          const uint16_t* vp = v_lds + ((kg * SUBS + sub) * 16 + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
+#pragma unroll
+          for (int nn = 0; nn < 8; ++nn)
+            o[nn] = mfma_16x16x16(lds_read_tr16(vp + 16 * nn), pb[sub], o[nn]);
+          psum = mfma_16x16x16(kOnesBf16x4, pb[sub], psum);
+        }
+      }
+      l = __builtin_fmaf(l, alpha, psum[0]);
+    };
+
+    // Every stage step runs in every round that has tiles beyond it (loads
+    // stay in one fixed order, so the compiler waits for exactly the stage it
+    // needs).  The last round issues no look-ahead loads: they would only hold
+    // the waves at their exit (sliding-window verify 7.2 -> 7.0 us).  Page ids
+    // are requested after the tile's products: with large pages they are
+    // scalar loads, which share the LDS reads' completion counter and return
+    // out of order, so a page id requested before the products would make
+    // their first LDS read wait for its whole memory round trip.
+    int t = t_begin;
+    for (; t + NS < t_end; t += NS) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        if constexpr (!WAVE_LOCAL) __syncthreads();
+        io.store(st[i], k_lds, v_lds);
+        if constexpr (!WAVE_LOCAL) __syncthreads();
+        // With wave-local tiles a wave issues its next loads at raised
+        // priority, ahead of the other waves' products on its SIMD, so the
+        // next tile is requested as soon as this one is in LDS (batched decode
+        // 37.5 -> 36.7 us; the shared 32- and 64-row tiles gain nothing).
+        if constexpr (WAVE_LOCAL) __builtin_amdgcn_s_setprio(1);
+        io.fetch_data(t + i + NS, pg[i], st[i]);
+        if constexpr (WAVE_LOCAL) __builtin_amdgcn_s_setprio(0);
+        compute_tile(t + i);
+        io.fetch_pages(t + i + 2 * NS, pg[i]);
       }
     }
-    l = __builtin_fmaf(l, alpha, psum[0]);
-  };
-
-  // Every stage step runs in every round that has tiles beyond it (loads
-  // stay in one fixed order, so the compiler waits for exactly the stage it
-  // needs).  The last round issues no look-ahead loads: they would only hold
-  // the waves at their exit (sliding-window verify 7.2 -> 7.0 us).  Page ids
-  // are requested after the tile's products: with large pages they are
-  // scalar loads, which share the LDS reads' completion counter and return
-  // out of order, so a page id requested before the products would make
-  // their first LDS read wait for its whole memory round trip.
-  int t = t_begin;
-  for (; t + NS < t_end; t += NS) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      if constexpr (!WAVE_LOCAL) __syncthreads();
-      io.store(st[i], k_lds, v_lds);
-      if constexpr (!WAVE_LOCAL) __syncthreads();
-      // With wave-local tiles a wave issues its next loads at raised
-      // priority, ahead of the other waves' products on its SIMD, so the
-      // next tile is requested as soon as this one is in LDS (batched decode
-      // 37.5 -> 36.7 us; the shared 32- and 64-row tiles gain nothing).
-      if constexpr (WAVE_LOCAL) __builtin_amdgcn_s_setprio(1);
-      io.fetch_data(t + i + NS, pg[i], st[i]);
-      if constexpr (WAVE_LOCAL) __builtin_amdgcn_s_setprio(0);
-      compute_tile(t + i);
-      io.fetch_pages(t + i + 2 * NS, pg[i]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    if (t + i < t_end) {                       // uniform over the workgroup
-      if constexpr (!WAVE_LOCAL) __syncthreads();
-      io.store(st[i], k_lds, v_lds);
-      if constexpr (!WAVE_LOCAL) __syncthreads();
-      compute_tile(t + i);
+      if (t + i < t_end) {                       // uniform over the workgroup
+        if constexpr (!WAVE_LOCAL) __syncthreads();
+        io.store(st[i], k_lds, v_lds);
+        if constexpr (!WAVE_LOCAL) __syncthreads();
+        compute_tile(t + i);
+      }
     }
   }
 
@@ -537,45 +710,53 @@ void split_attn_kernel(const SplitArgs a) {
       atomicAdd(a.count_out + (size_t)(r0 + tok) * a.hq + h, cnt);
   }
 
-  // Waves that split the keys of one row tile combine through LDS.
+  // Waves that split the keys of one row tile combine through LDS: each
+  // publishes its (m, l), scales its own O to the common reference and
+  // publishes it; then each of the KW waves sums and stores 8 / KW of the
+  // eight 16-column blocks, so the LDS reads, adds and output stores are
+  // spread over the waves instead of falling to one of them.
+  constexpr int NNW = 8 / KW;                  // column blocks a wave stores
+  int nn0 = 0;                                 // its first block
   if constexpr (KW > 1) {
-    constexpr int STR = 34;
-    static_assert(4 * 64 * STR * 4 <= (kKLdsElems<DQK> + kVLdsElems) * 2, "reduction fits");
+    constexpr int ML_ELEMS = 4 * 64 * 4;       // (m, l) per wave and lane, in uint16 units
+    constexpr int OB_ELEMS = 4 * 8 * 64 * 8;   // scaled O per wave, block and lane
+    static_assert(ML_ELEMS + OB_ELEMS + 4 * 64 * 2 <= kKLdsElems<DQK> + kVLdsElems, "reduction fits");
+    f32x2* ml = reinterpret_cast<f32x2*>(lds);
+    f32x4* ob = reinterpret_cast<f32x4*>(lds + ML_ELEMS);
+    __syncthreads();                           // every wave is done with its tiles
+    ml[wave * 64 + lane] = f32x2{m, l};
     __syncthreads();
-    float* red = reinterpret_cast<float*>(lds);
-    float* mine = red + (wave * 64 + lane) * STR;
-    mine[0] = m;
-    mine[1] = l;
+    float M = -INFINITY;
 #pragma unroll
-    for (int nn = 0; nn < 8; ++nn)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mine[2 + 4 * nn + i] = o[nn][i];
-    __syncthreads();
-    if (kg != 0) return;
-    float M = m;
-#pragma unroll
-    for (int k = 1; k < KW; ++k) M = fmaxf(M, red[((rt + k * RT) * 64 + lane) * STR]);
+    for (int k = 0; k < KW; ++k) M = fmaxf(M, ml[(rt + k * RT) * 64 + lane].x);
     const float M_use = M == -INFINITY ? 0.f : M;
-    const float f0 = fast_exp2(m - M_use);
-    l *= f0;
+    float L = 0.f;
 #pragma unroll
-    for (int nn = 0; nn < 8; ++nn) o[nn] *= f0;
+    for (int k = 0; k < KW; ++k) {
+      const f32x2 e = ml[(rt + k * RT) * 64 + lane];
+      L += fast_exp2(e.x - M_use) * e.y;
+    }
+    const float f = fast_exp2(m - M_use);
 #pragma unroll
-    for (int k = 1; k < KW; ++k) {
-      const float* other = red + ((rt + k * RT) * 64 + lane) * STR;
-      const float fk = fast_exp2(other[0] - M_use);
-      l += fk * other[1];
+    for (int nn = 0; nn < 8; ++nn) ob[(wave * 8 + nn) * 64 + lane] = o[nn] * f;
+    __syncthreads();
+    nn0 = kg * NNW;
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn)
+    for (int j = 0; j < NNW; ++j) {
+      f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[nn][i] += fk * other[2 + 4 * nn + i];
+      for (int k = 0; k < KW; ++k) sum += ob[((rt + k * RT) * 8 + nn0 + j) * 64 + lane];
+      o[j] = sum;
     }
     m = M;
+    l = L;
   }
 
-  if (!row_ok) return;
+  // o[j] now holds column block nn0 + j of this lane's row: dims
+  // 16 (nn0 + j) + 4 grp + 0..3.  The row's lse goes out once, from kg 0.
   const size_t out_row = (size_t)(r0 + tok) * a.hq + h;
   if (direct) {
+    if (!row_ok) return;
     float coef;
     if (a.sinks) {
       const float s2 = sink * kLog2e;
@@ -587,19 +768,19 @@ void split_attn_kernel(const SplitArgs a) {
     }
     coef *= a.v_scale;
     if (a.part_out) {
-      float* op = a.part_out + out_row * kHeadDimV + 4 * grp;
+      float* op = a.part_out + out_row * kHeadDimV + 16 * nn0 + 4 * grp;
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn) *reinterpret_cast<f32x4*>(op + 16 * nn) = o[nn] * coef;
-      if (grp == 0) a.lse_out[out_row] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+      for (int j = 0; j < NNW; ++j) *reinterpret_cast<f32x4*>(op + 16 * j) = o[j] * coef;
+      if (kg == 0 && grp == 0) a.lse_out[out_row] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
       return;
     }
-    uint16_t* op = a.out + out_row * kHeadDimV + 4 * grp;
+    uint16_t* op = a.out + out_row * kHeadDimV + 16 * nn0 + 4 * grp;
 #pragma unroll
-    for (int nn = 0; nn < 8; ++nn) {
-      const f32x4 v = o[nn] * coef;
-      *reinterpret_cast<u32x2*>(op + 16 * nn) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    for (int j = 0; j < NNW; ++j) {
+      const f32x4 v = o[j] * coef;
+      *reinterpret_cast<u32x2*>(op + 16 * j) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
-    if (a.lse_out && grp == 0) a.lse_out[out_row] = (m + log2f(l)) * kLn2;
+    if (a.lse_out && kg == 0 && grp == 0) a.lse_out[out_row] = (m + log2f(l)) * kLn2;
   } else {
     const size_t prow = prow0 + rt * 16 + col;
     // The normalised partial row (a convex combination of V rows) is stored
@@ -608,13 +789,24 @@ void split_attn_kernel(const SplitArgs a) {
     // Each element then keeps fp16's 11 bits relative to the row maximum,
     // so the merge adds far less than the output's own bf16 rounding (a bf16
     // partial would round every row twice at 8 bits), and any finite V fits.
+    // With the blocks spread over KW waves the row maximum meets in LDS.
     const float inv = l > 0.f ? 1.f / l : 0.f;
     float amax = 0.f;
 #pragma unroll
-    for (int nn = 0; nn < 8; ++nn)
+    for (int j = 0; j < NNW; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[nn][i]));
-    amax = max_over_lane_groups(amax) * inv;
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[j][i]));
+    amax = max_over_lane_groups(amax);
+    if constexpr (KW > 1) {
+      float* ab = reinterpret_cast<float*>(lds + 4 * 64 * 4 + 4 * 8 * 64 * 8);
+      ab[wave * 64 + lane] = amax;
+      __syncthreads();
+      amax = 0.f;
+#pragma unroll
+      for (int k = 0; k < KW; ++k) amax = fmaxf(amax, ab[(rt + k * RT) * 64 + lane]);
+    }
+    amax *= inv;
+    if (!row_ok) return;
     int e = 0;
     if (amax > 0.f) {
       int k;
@@ -622,16 +814,15 @@ void split_attn_kernel(const SplitArgs a) {
       e = max(k - 15, -100);                  // 2^-e stays a normal float
     }
     const float p2 = __builtin_amdgcn_ldexpf(1.f, -e);
-    uint16_t* pp = a.part_o + prow * kHeadDimV + 4 * grp;
+    uint16_t* pp = a.part_o + prow * kHeadDimV + 16 * nn0 + 4 * grp;
 #pragma unroll
-    for (int nn = 0; nn < 8; ++nn) {
-      const f32x4 v = (o[nn] * inv) * p2;
-      *reinterpret_cast<u32x2*>(pp + 16 * nn) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+    for (int j = 0; j < NNW; ++j) {
+      const f32x4 v = (o[j] * inv) * p2;
+      *reinterpret_cast<u32x2*>(pp + 16 * j) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
     }
-    if (grp == 0) a.part_lse[prow] = f32x2{l > 0.f ? m + log2f(l) : -INFINITY, (float)e};
+    if (kg == 0 && grp == 0) a.part_lse[prow] = f32x2{l > 0.f ? m + log2f(l) : -INFINITY, (float)e};
   }
 }
-
 
 // Combines the split partials of one query row: weights 2^(lse_s - M) (times
 // 2^e_s on the stored fp16 row), the sink joining the denominator, v_scale,
