@@ -47,9 +47,10 @@ class Case:
     spare block-table rows, spare q / out rows) and valid page ids in every
     block-table entry."""
 
-    def __init__(self, seed=5, kv_dtype="bf16"):
+    def __init__(self, seed=5, kv_dtype="bf16", window=0):
         inp = make_paged_inputs(seed, seq_lens=[700, 1300, 520], q_lens=[8, 5, 8], num_q_heads=8,
-                                num_kv_heads=1, page_size=16, kv_dtype=kv_dtype, sinks=True)
+                                num_kv_heads=1, page_size=16, kv_dtype=kv_dtype, sinks=True,
+                                window=window, write_align=16 if window else None)
         self.inp = inp
         self.dev = DeviceInputs(inp)
         dev = self.dev
@@ -86,10 +87,10 @@ class Case:
 CALLS = [("verify", 3), ("verify", 1), ("prefill", 0), ("mixed", 0)]
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
-def test_valid_inputs_match_the_release_build_and_flag_nothing(kv_dtype):
-    print(f"[gpu] debug build on valid inputs ({kv_dtype})", flush=True)
-    case = Case(kv_dtype=kv_dtype)
+@pytest.mark.parametrize("kv_dtype,window", [("bf16", 0), ("fp8", 0), ("fp8", 100)])
+def test_valid_inputs_match_the_release_build_and_flag_nothing(kv_dtype, window):
+    print(f"[gpu] debug build on valid inputs ({kv_dtype}, window {window})", flush=True)
+    case = Case(kv_dtype=kv_dtype, window=window)
     release = [case.call(e, case.desc(s)) for e, s in CALLS]
     B.select_library("debug")
     try:
@@ -118,6 +119,16 @@ def test_block_table_entry_past_the_pool_is_flagged(debug_library):
     case = Case()
     case.bt[1, 3] = case.inp.num_pages + 3                # a visible page; a spare page exists there
     for f in run_flags(case, case.desc(0)):
+        assert f & PAGES, f
+
+
+def test_block_table_entry_past_the_pool_is_flagged_in_a_short_window(debug_library):
+    # A window of 100 keys spans at most three 64-key tiles: the one-chunk
+    # launch's short-range pass reads the block table itself.
+    print("[gpu] debug build: block-table entry past the pool, short window", flush=True)
+    case = Case(window=100)
+    case.bt[1, (1300 - 1) // 16] = case.inp.num_pages + 3    # the last page of sequence 1
+    for f in run_flags(case, case.desc(0), calls=[("verify", 0)]):
         assert f & PAGES, f
 
 
