@@ -25,7 +25,10 @@
 // Keeping S and O transposed puts one query row in each lane, so the softmax
 // rescale needs no data movement between lanes.
 // The global loads of the next NS tiles are in flight in registers while a
-// tile is converted into LDS and multiplied.
+// tile is converted into LDS and multiplied.  A one-chunk launch whose pairs
+// span at most four tiles (sliding windows, short sequences) takes the
+// short-range pass instead: all of a pair's loads at once, K straight into
+// the MFMA operands, one softmax update.
 #pragma once
 
 #include <type_traits>
