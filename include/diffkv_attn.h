@@ -321,6 +321,23 @@ int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t wind
  * enqueue nothing; NULL flags is DIFFKV_INVALID_ARGUMENT. */
 int diffkv_attn_debug_flags(uint32_t* flags, hipStream_t stream);
 
+/* Timeline builds only (the library compiled with -DDIFFKV_TIMELINE, shipped
+ * as libdiffkv_attn_timeline.so; a measurement tool, not for production
+ * calls).  Their split-KV kernels stamp the shader real-time counter (100
+ * MHz) at eight points of each workgroup's work: 0 start, 1 lengths (and
+ * the plan's totals) in, 2 own key range known, 3 first K/V data in (the
+ * short-range pass: all of K), 4 first tile done (the short-range pass: its
+ * products done), 5 last round of the tile loop, 6 epilogue, 7 output
+ * stores issued.  A workgroup that finishes a chunk writes its eight stamps
+ * to stamps[8 w .. 8 w + 7], w = blockIdx.y * gridDim.x + blockIdx.x, while
+ * 8 w + 7 < entries, the stamps it did not pass as 0.  This call
+ * registers the caller's device buffer (NULL with entries 0 turns the
+ * writes off) for the current device, synchronously, so it must not be
+ * captured into a graph; the buffer must stay valid while timed calls run.
+ * Other builds return DIFFKV_UNSUPPORTED; exactly one of stamps == NULL and
+ * entries == 0 is DIFFKV_INVALID_ARGUMENT. */
+int diffkv_attn_timeline_buffer(uint64_t* stamps, size_t entries);
+
 /* Static text for a status code. */
 const char* diffkv_attn_strerror(int status);
 

@@ -30,7 +30,8 @@ class AttnDesc(ctypes.Structure):
         "force_num_splits")] + [("profile_start", ctypes.c_void_p), ("profile_stop", ctypes.c_void_p)]
 
 
-_LIBRARY_FILES = {"release": "libdiffkv_attn.so", "debug": "libdiffkv_attn_debug.so"}
+_LIBRARY_FILES = {"release": "libdiffkv_attn.so", "debug": "libdiffkv_attn_debug.so",
+                  "timeline": "libdiffkv_attn_timeline.so"}
 _VARIANT = "release"
 
 
@@ -39,9 +40,11 @@ def library_path():
 
 
 def select_library(variant):
-    """Which build later calls open: "release" (the default) or "debug" (the
+    """Which build later calls open: "release" (the default), "debug" (the
     same library with the device-side precondition checks compiled in; see
-    diffkv_attn_debug_flags).  Calls prepared earlier keep their library."""
+    diffkv_attn_debug_flags) or "timeline" (with per-workgroup real-time
+    stamps in the split-KV kernels; see diffkv_attn_timeline_buffer).  Calls
+    prepared earlier keep their library."""
     global _VARIANT, _LIB
     if variant not in _LIBRARY_FILES:
         raise ValueError(f"unknown library variant {variant!r}")
@@ -89,6 +92,8 @@ def load_library():
     lib.diffkv_attn_num_splits.restype = ctypes.c_int
     lib.diffkv_attn_debug_flags.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.diffkv_attn_debug_flags.restype = ctypes.c_int
+    lib.diffkv_attn_timeline_buffer.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.diffkv_attn_timeline_buffer.restype = ctypes.c_int
     lib.diffkv_attn_strerror.argtypes = [ctypes.c_int]
     lib.diffkv_attn_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -134,6 +139,15 @@ def diffkv_attn_debug_flags(flags, stream=None):
     one-element int32 device tensor) and clear them; returns the status
     (UNSUPPORTED from a release build, which enqueues nothing)."""
     return int(load_library().diffkv_attn_debug_flags(_ptr(flags), _stream(stream)))
+
+
+def diffkv_attn_timeline_buffer(stamps):
+    """Register a uint64/int64 device tensor for the timeline build's stamps
+    (eight per workgroup), or None to turn them off; returns the status
+    (UNSUPPORTED from other builds).  Synchronous; not for graph capture."""
+    if stamps is None:
+        return int(load_library().diffkv_attn_timeline_buffer(None, 0))
+    return int(load_library().diffkv_attn_timeline_buffer(_ptr(stamps), stamps.numel()))
 
 
 def set_profile_events(desc, start, stop):

@@ -1,7 +1,9 @@
 """Builds libdiffkv_attn.so (the attention library), libdiffkv_attn_debug.so
 (the same library with the device-side precondition checks compiled in,
--DDIFFKV_DEBUG) and libdiffkv_stream.so (the streaming-read reference the
-benchmark quotes beside HBM peak) in-tree with hipcc for gfx950.
+-DDIFFKV_DEBUG), libdiffkv_attn_timeline.so (the same with per-workgroup
+real-time stamps in the split-KV kernels, -DDIFFKV_TIMELINE) and
+libdiffkv_stream.so (the streaming-read reference the benchmark quotes
+beside HBM peak) in-tree with hipcc for gfx950.
 
     python -m paged_asymmetric_head_amd.build
 
@@ -19,6 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUTPUT = os.path.join(HERE, "libdiffkv_attn.so")
 DEBUG_OUTPUT = os.path.join(HERE, "libdiffkv_attn_debug.so")
+TIMELINE_OUTPUT = os.path.join(HERE, "libdiffkv_attn_timeline.so")
 SOURCES = [os.path.join(CSRC, "diffkv_attn.hip")]
 STREAM_OUTPUT = os.path.join(HERE, "libdiffkv_stream.so")
 STREAM_SOURCES = [os.path.join(CSRC, "stream_read.hip")]
@@ -55,6 +58,7 @@ def build(verbose=False):
     """Compile the libraries; returns the attention library's path."""
     _compile(OUTPUT, SOURCES, verbose)
     _compile(DEBUG_OUTPUT, SOURCES, verbose, extra=("-DDIFFKV_DEBUG",))
+    _compile(TIMELINE_OUTPUT, SOURCES, verbose, extra=("-DDIFFKV_TIMELINE",))
     _compile(STREAM_OUTPUT, STREAM_SOURCES, verbose)
     return OUTPUT
 

@@ -212,6 +212,56 @@ __device__ __forceinline__ void debug_flag(uint32_t bits) { atomicOr(&g_debug_fl
 // Value of x in lane `lane` (wave-uniform) for every lane.
 __device__ __forceinline__ int read_lane(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
 
+// Timeline builds (-DDIFFKV_TIMELINE, shipped as libdiffkv_attn_timeline.so)
+// stamp the shader real-time counter (100 MHz) at fixed points of the split
+// kernel: thread 0 keeps kTlSlots stamps in LDS (zero until stamped) and
+// writes them out when its workgroup finishes a chunk, to slot (blockIdx.y * gridDim.x + blockIdx.x) *
+// kTlSlots of a buffer registered with diffkv_attn_timeline_buffer.  A stamp
+// after a value waits for that value (the empty asm takes it as an operand).
+// In other builds the macros expand to nothing.
+constexpr int kTlSlots = 8;
+#ifdef DIFFKV_TIMELINE
+__device__ uint64_t* g_tl_buf;
+__device__ uint64_t g_tl_entries;
+__shared__ uint64_t g_tl_stamps[kTlSlots];
+#define DIFFKV_STAMP(k)                                                              \
+  do {                                                                               \
+    if (threadIdx.x == 0) ::diffkv::g_tl_stamps[k] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define DIFFKV_STAMP_AFTER(k, v)         \
+  do {                                   \
+    asm volatile("" ::"v"(v));           \
+    DIFFKV_STAMP(k);                     \
+  } while (0)
+#define DIFFKV_STAMP_BEGIN()                                                       \
+  do {                                                                             \
+    if (threadIdx.x == 0)                                                          \
+      for (int k_ = 1; k_ < ::diffkv::kTlSlots; ++k_) ::diffkv::g_tl_stamps[k_] = 0; \
+    DIFFKV_STAMP(0);                                                               \
+  } while (0)
+#define DIFFKV_STAMP_FLUSH()                                                                      \
+  do {                                                                                            \
+    if (threadIdx.x == 0 && ::diffkv::g_tl_buf) {                                                 \
+      const uint64_t w_ = ((uint64_t)blockIdx.y * gridDim.x + blockIdx.x) * ::diffkv::kTlSlots;   \
+      for (int k_ = 0; k_ < ::diffkv::kTlSlots; ++k_)                                             \
+        if (w_ + k_ < ::diffkv::g_tl_entries) ::diffkv::g_tl_buf[w_ + k_] = ::diffkv::g_tl_stamps[k_]; \
+    }                                                                                             \
+  } while (0)
+#else
+#define DIFFKV_STAMP_BEGIN() \
+  do {                       \
+  } while (0)
+#define DIFFKV_STAMP(k) \
+  do {                  \
+  } while (0)
+#define DIFFKV_STAMP_AFTER(k, v) \
+  do {                           \
+  } while (0)
+#define DIFFKV_STAMP_FLUSH() \
+  do {                       \
+  } while (0)
+#endif
+
 // Packed query row where sequence b starts: sum of q_lens[0..b).  One wave
 // computes it cooperatively (a strided sum and a wave reduction).
 __device__ __forceinline__ int seq_row_start(const int32_t* q_lens, int b) {

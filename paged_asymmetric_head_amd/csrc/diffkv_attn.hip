@@ -518,6 +518,21 @@ int diffkv_attn_num_splits(const diffkv_attn_desc* desc, int entry, int32_t wind
       .max_chunks;
 }
 
+int diffkv_attn_timeline_buffer(uint64_t* stamps, size_t entries) {
+#ifdef DIFFKV_TIMELINE
+  if ((stamps == nullptr) != (entries == 0)) return DIFFKV_INVALID_ARGUMENT;
+  const uint64_t n = entries;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_tl_buf), &stamps, sizeof(stamps)) != hipSuccess ||
+      hipMemcpyToSymbol(HIP_SYMBOL(g_tl_entries), &n, sizeof(n)) != hipSuccess)
+    return DIFFKV_HIP_ERROR;
+  return DIFFKV_OK;
+#else
+  (void)stamps;
+  (void)entries;
+  return DIFFKV_UNSUPPORTED;
+#endif
+}
+
 int diffkv_attn_debug_flags(uint32_t* flags, hipStream_t stream) {
 #ifdef DIFFKV_DEBUG
   if (flags == nullptr) return DIFFKV_INVALID_ARGUMENT;

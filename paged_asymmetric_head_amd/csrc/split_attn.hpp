@@ -356,6 +356,7 @@ __device__ __forceinline__ void window_pass(const SplitArgs& a, int b, int g, in
     for (int u = 0; u < VL; ++u) vr[i][u] = *reinterpret_cast<const u32x4*>(rv ? vp + 16 * u : g_zero_row);
   }
 
+  DIFFKV_STAMP_AFTER(3, kr[kWinTiles - 1][KL - 1].x);
   // S^T of every tile: independent MFMA chains.
   f32x4 sacc[kWinTiles];
 #pragma unroll
@@ -431,6 +432,7 @@ __device__ __forceinline__ void window_pass(const SplitArgs& a, int b, int g, in
     psum = mfma_16x16x32(kOnesBf16x8, pt, psum);
   }
   l = psum[0];
+  DIFFKV_STAMP_AFTER(4, l);
 }
 
 template <bool FP8, int RT, bool DIRECT, bool COUNT, bool UPAGE, int NS, int DQK>
@@ -456,6 +458,7 @@ void split_attn_kernel(const SplitArgs a) {
   uint16_t* k_lds = lds;
   uint16_t* v_lds = lds + kKLdsElems<DQK>;
 
+  DIFFKV_STAMP_BEGIN();
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -480,9 +483,11 @@ void split_attn_kernel(const SplitArgs a) {
     // loads, its own loads waited for the tile in the in-order load counter
     // and put the query rows a round trip behind it).
     r0 = seq_row_start(a.q_lens, b);
+    DIFFKV_STAMP_AFTER(1, L + r0);
   } else {
     SplitPlanner<ROWS> plan(a, gdiv);
     plan.init();
+    DIFFKV_STAMP_AFTER(1, plan.C);
     if (!plan.find(blockIdx.x, b, qt, c, base, k, L, n, klo, khi, r0) || base + c >= a.chunk_bound)
       return;
     // The pair's first chunk records where the merge finds the pair.
@@ -494,6 +499,7 @@ void split_attn_kernel(const SplitArgs a) {
   int kv_lo, kv_hi, t_begin = 0, t_end = 0;
   pair_key_range(L, n, gdiv, qt, ROWS, a.window, klo, khi, kv_lo, kv_hi);
   if (kv_hi > kv_lo) split_tiles(kv_lo, kv_hi, k, c, t_begin, t_end);
+  DIFFKV_STAMP_AFTER(2, t_end);
   // Partial row of this chunk for row r of the tile.
   const size_t prow0 = ((size_t)(base + c) * a.hkv + g) * ROWS;
   if (t_begin >= t_end) {
@@ -678,6 +684,7 @@ void split_attn_kernel(const SplitArgs a) {
     // out of order, so a page id requested before the products would make
     // their first LDS read wait for its whole memory round trip.
     int t = t_begin;
+    DIFFKV_STAMP_AFTER(3, st[0].k[0].x);
     for (; t + NS < t_end; t += NS) {
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
@@ -692,9 +699,11 @@ void split_attn_kernel(const SplitArgs a) {
         io.fetch_data(t + i + NS, pg[i], st[i]);
         if constexpr (WAVE_LOCAL) __builtin_amdgcn_s_setprio(0);
         compute_tile(t + i);
+        if (t + i == t_begin) DIFFKV_STAMP(4);
         io.fetch_pages(t + i + 2 * NS, pg[i]);
       }
     }
+    DIFFKV_STAMP(5);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (t + i < t_end) {                       // uniform over the workgroup
@@ -706,6 +715,7 @@ void split_attn_kernel(const SplitArgs a) {
     }
   }
 
+  DIFFKV_STAMP(6);
   if constexpr (COUNT) {
     cnt += __shfl_xor(cnt, 16, 64);
     cnt += __shfl_xor(cnt, 32, 64);
@@ -775,6 +785,8 @@ void split_attn_kernel(const SplitArgs a) {
 #pragma unroll
       for (int j = 0; j < NNW; ++j) *reinterpret_cast<f32x4*>(op + 16 * j) = o[j] * coef;
       if (kg == 0 && grp == 0) a.lse_out[out_row] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+      DIFFKV_STAMP(7);
+      DIFFKV_STAMP_FLUSH();
       return;
     }
     uint16_t* op = a.out + out_row * kHeadDimV + 16 * nn0 + 4 * grp;
@@ -784,6 +796,8 @@ void split_attn_kernel(const SplitArgs a) {
       *reinterpret_cast<u32x2*>(op + 16 * j) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
     if (a.lse_out && kg == 0 && grp == 0) a.lse_out[out_row] = (m + log2f(l)) * kLn2;
+    DIFFKV_STAMP(7);
+    DIFFKV_STAMP_FLUSH();
   } else {
     const size_t prow = prow0 + rt * 16 + col;
     // The normalised partial row (a convex combination of V rows) is stored
@@ -824,6 +838,8 @@ void split_attn_kernel(const SplitArgs a) {
       *reinterpret_cast<u32x2*>(pp + 16 * j) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
     }
     if (kg == 0 && grp == 0) a.part_lse[prow] = f32x2{l > 0.f ? m + log2f(l) : -INFINITY, (float)e};
+    DIFFKV_STAMP(7);
+    DIFFKV_STAMP_FLUSH();
   }
 }
 

@@ -59,6 +59,24 @@ def test_release_library_has_no_debug_checks(lib):
     assert lib.diffkv_attn_debug_flags(None, None) == B.UNSUPPORTED
 
 
+def test_timeline_library_exports_every_declared_symbol():
+    """The timeline build (per-workgroup real-time stamps) has the same ABI;
+    its buffer call rejects a pointer / size mismatch before touching the
+    GPU, and the release build has no stamps."""
+    path = os.path.join(ROOT, "paged_asymmetric_head_amd", "libdiffkv_attn_timeline.so")
+    if not os.path.exists(path):
+        pytest.fail("libdiffkv_attn_timeline.so is not built (run __graft_entry__.build())")
+    tlib = ctypes.CDLL(path)
+    for name in declared_functions():
+        assert hasattr(tlib, name), name
+    tlib.diffkv_attn_timeline_buffer.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    assert tlib.diffkv_attn_timeline_buffer(None, 8) == B.INVALID_ARGUMENT
+
+
+def test_release_library_has_no_timeline(lib):
+    assert lib.diffkv_attn_timeline_buffer(None, 0) == B.UNSUPPORTED
+
+
 def good_desc(**kw):
     d = dict(batch=4, num_q_heads=8, num_kv_heads=1, head_dim_qk=192, head_dim_v=128,
              page_size=128, num_pages=2000, block_table_stride=400, max_seq_len=50000,
