@@ -454,7 +454,13 @@ void split_attn_kernel(const SplitArgs a) {
   constexpr int LDS_ELEMS = DIRECT && WAVE_LOCAL && kWinTiles * kVLdsElems > kKLdsElems<DQK> + kVLdsElems
                                 ? kWinTiles * kVLdsElems
                                 : kKLdsElems<DQK> + kVLdsElems;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+  // Waves that split the keys of a row tile combine in a region of their
+  // own, so none has to wait for the others' last tile before writing:
+  // (m, l, row max of |O|) and the unscaled O per wave and lane.
+  constexpr int ML_ELEMS = 4 * 64 * 8;         // f32x4 per wave and lane, in uint16 units
+  constexpr int OB_ELEMS = 4 * 8 * 64 * 8;     // f32x4 per wave, column block and lane
+  constexpr int COMB_ELEMS = KW > 1 ? ML_ELEMS + OB_ELEMS : 0;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS + COMB_ELEMS];
   uint16_t* k_lds = lds;
   uint16_t* v_lds = lds + kKLdsElems<DQK>;
 
@@ -724,45 +730,54 @@ void split_attn_kernel(const SplitArgs a) {
   }
 
   // Waves that split the keys of one row tile combine through LDS: each
-  // publishes its (m, l), scales its own O to the common reference and
-  // publishes it; then each of the KW waves sums and stores 8 / KW of the
-  // eight 16-column blocks, so the LDS reads, adds and output stores are
-  // spread over the waves instead of falling to one of them.
+  // publishes its (m, l), the row maximum of its |O| and its O; after one
+  // barrier each of the KW waves weights and sums 8 / KW of the eight
+  // 16-column blocks for its rows and stores them, so the reads, adds and
+  // output stores are spread over the waves.  The published row maxima give
+  // the partial rows' fp16 exponent a bound (the combined row's largest
+  // magnitude is at most sum_k f_k max|O_k|) without a second exchange.
   constexpr int NNW = 8 / KW;                  // column blocks a wave stores
   int nn0 = 0;                                 // its first block
+  float amax_bound = 0.f;                      // bound on the row's max |O| (KW > 1)
   if constexpr (KW > 1) {
-    constexpr int ML_ELEMS = 4 * 64 * 4;       // (m, l) per wave and lane, in uint16 units
-    constexpr int OB_ELEMS = 4 * 8 * 64 * 8;   // scaled O per wave, block and lane
-    static_assert(ML_ELEMS + OB_ELEMS + 4 * 64 * 2 <= kKLdsElems<DQK> + kVLdsElems, "reduction fits");
-    f32x2* ml = reinterpret_cast<f32x2*>(lds);
-    f32x4* ob = reinterpret_cast<f32x4*>(lds + ML_ELEMS);
-    __syncthreads();                           // every wave is done with its tiles
-    ml[wave * 64 + lane] = f32x2{m, l};
+    f32x4* ml = reinterpret_cast<f32x4*>(lds + LDS_ELEMS);
+    f32x4* ob = reinterpret_cast<f32x4*>(lds + LDS_ELEMS + ML_ELEMS);
+    float am = 0.f;
+    if (!direct) {
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) am = fmaxf(am, fabsf(o[nn][i]));
+      am = max_over_lane_groups(am);
+    }
+    ml[wave * 64 + lane] = f32x4{m, l, am, 0.f};
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) ob[(wave * 8 + nn) * 64 + lane] = o[nn];
     __syncthreads();
     float M = -INFINITY;
 #pragma unroll
     for (int k = 0; k < KW; ++k) M = fmaxf(M, ml[(rt + k * RT) * 64 + lane].x);
     const float M_use = M == -INFINITY ? 0.f : M;
-    float L = 0.f;
+    float f[KW];
+    float L = 0.f, A = 0.f;
 #pragma unroll
     for (int k = 0; k < KW; ++k) {
-      const f32x2 e = ml[(rt + k * RT) * 64 + lane];
-      L += fast_exp2(e.x - M_use) * e.y;
+      const f32x4 e = ml[(rt + k * RT) * 64 + lane];
+      f[k] = fast_exp2(e.x - M_use);
+      L += f[k] * e.y;
+      A += f[k] * e.z;
     }
-    const float f = fast_exp2(m - M_use);
-#pragma unroll
-    for (int nn = 0; nn < 8; ++nn) ob[(wave * 8 + nn) * 64 + lane] = o[nn] * f;
-    __syncthreads();
     nn0 = kg * NNW;
 #pragma unroll
     for (int j = 0; j < NNW; ++j) {
       f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < KW; ++k) sum += ob[((rt + k * RT) * 8 + nn0 + j) * 64 + lane];
+      for (int k = 0; k < KW; ++k) sum += f[k] * ob[((rt + k * RT) * 8 + nn0 + j) * 64 + lane];
       o[j] = sum;
     }
     m = M;
     l = L;
+    amax_bound = A;
   }
 
   // o[j] now holds column block nn0 + j of this lane's row: dims
@@ -806,21 +821,15 @@ void split_attn_kernel(const SplitArgs a) {
     // Each element then keeps fp16's 11 bits relative to the row maximum,
     // so the merge adds far less than the output's own bf16 rounding (a bf16
     // partial would round every row twice at 8 bits), and any finite V fits.
-    // With the blocks spread over KW waves the row maximum meets in LDS.
+    // With the blocks spread over KW waves, e comes from the bound above.
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float amax = 0.f;
+    float amax = amax_bound;
+    if constexpr (KW == 1) {
 #pragma unroll
-    for (int j = 0; j < NNW; ++j)
+      for (int j = 0; j < NNW; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[j][i]));
-    amax = max_over_lane_groups(amax);
-    if constexpr (KW > 1) {
-      float* ab = reinterpret_cast<float*>(lds + 4 * 64 * 4 + 4 * 8 * 64 * 8);
-      ab[wave * 64 + lane] = amax;
-      __syncthreads();
-      amax = 0.f;
-#pragma unroll
-      for (int k = 0; k < KW; ++k) amax = fmaxf(amax, ab[(rt + k * RT) * 64 + lane]);
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[j][i]));
+      amax = max_over_lane_groups(amax);
     }
     amax *= inv;
     if (!row_ok) return;
