@@ -284,11 +284,12 @@ struct SplitPlanner {
 // query rows are loaded with the same assignment of dims to contraction
 // steps (S^T = K Q^T only needs both operands to agree), so K makes no LDS
 // round trip.  V goes through LDS for the transposing reads, one region per
-// tile.  Slots past the pair's last tile, and keys outside [kv_lo, kv_hi),
-// read the zero row; the row masks drop every key a row does not see.
+// tile.  NT slots (the pair's tiles; one tile takes two): a slot past the
+// pair's last tile, and keys outside [kv_lo, kv_hi), read the zero row; the
+// row masks drop every key a row does not see.
 constexpr int kWinTiles = 4;
 
-template <bool FP8, bool UPAGE, bool COUNT, int DQK>
+template <bool FP8, bool UPAGE, bool COUNT, int DQK, int NT>
 __device__ __forceinline__ void window_pass(const SplitArgs& a, int b, int g, int kv_lo, int kv_hi,
                                             int t_begin, int t_end, int wave, int lane,
                                             const uint16_t* q_row, bool row_ok, int lo_row, int hi_row,
@@ -310,9 +311,10 @@ __device__ __forceinline__ void window_pass(const SplitArgs& a, int b, int g, in
   const int k_key = 16 * wave + col, v_key = 16 * wave + (lane >> 2), v_piece = lane & 3;
   auto readable = [&](int i, int j) { return i < nt && j >= kv_lo && j < kv_hi; };
 
-  int pk[kWinTiles], pv[kWinTiles];
+  static_assert(NT >= 1 && NT <= kWinTiles, "slots of the short-range pass");
+  int pk[NT], pv[NT];
 #pragma unroll
-  for (int i = 0; i < kWinTiles; ++i) {
+  for (int i = 0; i < NT; ++i) {
     const int t = min(t_begin + i, t_end - 1);
     if constexpr (UPAGE) {
       pk[i] = scalar_load(bt, (t * kTileKeys) >> lp);   // a tile lies inside one page
@@ -338,9 +340,9 @@ __device__ __forceinline__ void window_pass(const SplitArgs& a, int b, int g, in
                                                      : g_zero_row);
   // Every K load, then every V load: the products wait for K alone (loads
   // complete in issue order), and V arrives while QK^T and the softmax run.
-  u32x4 kr[kWinTiles][KL], vr[kWinTiles][VL];
+  u32x4 kr[NT][KL], vr[NT][VL];
 #pragma unroll
-  for (int i = 0; i < kWinTiles; ++i) {
+  for (int i = 0; i < NT; ++i) {
     const int jk = (t_begin + i) * kTileKeys + k_key;
     const uint8_t* kp = k_head + (((size_t)pk[i] << lp) | (size_t)(jk & pmask)) * k_slot + KD * grp * ESZ;
     const bool rk = readable(i, jk);
@@ -348,7 +350,7 @@ __device__ __forceinline__ void window_pass(const SplitArgs& a, int b, int g, in
     for (int u = 0; u < KL; ++u) kr[i][u] = *reinterpret_cast<const u32x4*>(rk ? kp + 16 * u : g_zero_row);
   }
 #pragma unroll
-  for (int i = 0; i < kWinTiles; ++i) {
+  for (int i = 0; i < NT; ++i) {
     const int jv = (t_begin + i) * kTileKeys + v_key;
     const uint8_t* vp = v_head + (((size_t)pv[i] << lp) | (size_t)(jv & pmask)) * v_slot + 32 * v_piece * ESZ;
     const bool rv = readable(i, jv);
@@ -356,15 +358,15 @@ __device__ __forceinline__ void window_pass(const SplitArgs& a, int b, int g, in
     for (int u = 0; u < VL; ++u) vr[i][u] = *reinterpret_cast<const u32x4*>(rv ? vp + 16 * u : g_zero_row);
   }
 
-  DIFFKV_STAMP_AFTER(3, kr[kWinTiles - 1][KL - 1].x);
+  DIFFKV_STAMP_AFTER(3, kr[NT - 1][KL - 1].x);
   // S^T of every tile: independent MFMA chains.
-  f32x4 sacc[kWinTiles];
+  f32x4 sacc[NT];
 #pragma unroll
-  for (int i = 0; i < kWinTiles; ++i) sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NT; ++i) sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < QC; ++c)
 #pragma unroll
-    for (int i = 0; i < kWinTiles; ++i) {
+    for (int i = 0; i < NT; ++i) {
       u32x4 kf;
       if constexpr (FP8) {
         const uint32_t w0 = (c & 1) ? kr[i][c >> 1].z : kr[i][c >> 1].x;
@@ -379,7 +381,7 @@ __device__ __forceinline__ void window_pass(const SplitArgs& a, int b, int g, in
   // sacc[i][r] = raw score of key (t_begin + i) * 64 + 16 wave + 4 grp + r.
   float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kWinTiles; ++i)
+  for (int i = 0; i < NT; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = (t_begin + i) * kTileKeys + 16 * wave + 4 * grp + r;
@@ -392,9 +394,9 @@ __device__ __forceinline__ void window_pass(const SplitArgs& a, int b, int g, in
   const float scale = a.scale_log2;
   m = next_reference(-INFINITY, mx * scale);
   const float m_use = m == -INFINITY ? 0.f : m;
-  u32x2 pb[kWinTiles];
+  u32x2 pb[NT];
 #pragma unroll
-  for (int i = 0; i < kWinTiles; ++i) {
+  for (int i = 0; i < NT; ++i) {
     float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(__builtin_fmaf(sacc[i][r], scale, -m_use));
@@ -404,7 +406,7 @@ __device__ __forceinline__ void window_pass(const SplitArgs& a, int b, int g, in
   // V rows into LDS (bf16, row-major), this wave's 16 rows of each tile's
   // region; only this wave reads them, so program order suffices.
 #pragma unroll
-  for (int i = 0; i < kWinTiles; ++i) {
+  for (int i = 0; i < NT; ++i) {
     uint16_t* dst = v_lds + i * kVLdsElems + v_key * kVLdsStride + 32 * v_piece;
 #pragma unroll
     for (int u = 0; u < VL; ++u) {
@@ -420,12 +422,21 @@ __device__ __forceinline__ void window_pass(const SplitArgs& a, int b, int g, in
   }
 
   // O^T = V^T P^T over two tiles' 16 keys per step (32 keys, as the loop's
-  // paired subtiles), the row sums from the all-ones tile.
+  // paired subtiles; an odd last tile alone), the row sums from the all-ones
+  // tile.
   f32x4 psum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < kWinTiles; i += 2) {
-    const u32x4 pt = cat(pb[i], pb[i + 1]);
+  for (int i = 0; i < NT; i += 2) {
     const uint16_t* vp = v_lds + i * kVLdsElems + (16 * wave + 4 * grp + (col >> 2)) * kVLdsStride + 4 * (col & 3);
+    if constexpr (NT % 2 == 1) {
+      if (i + 1 == NT) {
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn) o[nn] = mfma_16x16x16(lds_read_tr16(vp + 16 * nn), pb[i], o[nn]);
+        psum = mfma_16x16x16(kOnesBf16x4, pb[i], psum);
+        break;
+      }
+    }
+    const u32x4 pt = cat(pb[i], pb[min(i + 1, NT - 1)]);
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn)
       o[nn] = mfma_16x16x32(cat(lds_read_tr16(vp + 16 * nn), lds_read_tr16(vp + kVLdsElems + 16 * nn)), pt, o[nn]);
@@ -552,9 +563,17 @@ void split_attn_kernel(const SplitArgs a) {
   bool windowed = false;
   if constexpr (DIRECT && WAVE_LOCAL) windowed = t_end - t_begin <= kWinTiles;   // uniform
   if (windowed) {
-    window_pass<FP8, UPAGE, COUNT, DQK>(a, b, g, kv_lo, kv_hi, t_begin, t_end, wave, lane,
-                                        a.q + ((size_t)(r0 + tok) * a.hq + h) * DQK, row_ok, lo_row,
-                                        hi_row, lds, m, l, o, cnt);
+    // Only the pair's own tiles are multiplied (a window of 128 keys spans
+    // three tiles unless it starts in a tile's last two keys).
+    auto pass = [&](auto nt) {
+      window_pass<FP8, UPAGE, COUNT, DQK, decltype(nt)::value>(
+          a, b, g, kv_lo, kv_hi, t_begin, t_end, wave, lane, a.q + ((size_t)(r0 + tok) * a.hq + h) * DQK,
+          row_ok, lo_row, hi_row, lds, m, l, o, cnt);
+    };
+    const int nt = t_end - t_begin;         // 1 .. kWinTiles, uniform
+    if (nt <= 2) pass(std::integral_constant<int, 2>{});
+    else if (nt == 3) pass(std::integral_constant<int, 3>{});
+    else pass(std::integral_constant<int, 4>{});
   } else {
     const IO io(a.k_cache, a.v_cache, a.block_table + (size_t)b * a.bt_stride, a.hkv, g,
                 a.log2_page, kv_lo, kv_hi, t_end, WAVE_LOCAL ? lane : tid, WAVE_LOCAL ? 16 * wave : 0,
