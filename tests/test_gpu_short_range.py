@@ -4,7 +4,10 @@ operands, one softmax update) against the FP64 oracle, at the edges of its
 tile arithmetic: windows whose first key sits at offsets 0, 1, 62 and 63 of a
 tile (three and four tiles), a window of one key, the widest span that still
 fits four tiles, 16-token blocks at GQA 16 (sixteen 16-row query tiles per
-pair), symmetric 128-wide heads, bf16 and FP8, pages of 1, 16 and 128.
+pair), symmetric 128-wide heads, bf16 and FP8, pages of 1, 16 and 128.  The
+pass is compiled for two, three and four tile slots (a pair of one tile takes
+two, the second reading the zero row; three slots multiply the last tile's
+keys alone); each count is covered in both formats.
 Every row, its log-sum-exp and its visible-key count are compared."""
 
 import pytest
@@ -32,6 +35,12 @@ CASES = [
     (16, window_case(40, 100, 16), 16, 16, 1, 100, True, "fp8", 192),
     (1, window_case(63, 128, 4), 4, 8, 2, 128, True, "fp8", 128),
     (16, [37, 200, 3, 256], 3, 8, 1, 0, False, "bf16", 128),
+    # two tiles (sequences of 65-128 keys, no window), then three tiles in
+    # bf16 and with 128-wide heads
+    (128, [100, 90, 128, 65], 1, 8, 1, 0, True, "bf16", 192),
+    (16, [70, 127, 66], 2, 8, 2, 0, False, "fp8", 192),
+    (16, window_case(10, 128, 4), 4, 8, 1, 128, True, "bf16", 192),
+    (1, window_case(20, 128, 4), 4, 8, 2, 128, False, "bf16", 128),
 ]
 
 
